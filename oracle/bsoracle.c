@@ -1,0 +1,370 @@
+/*
+ * bsoracle.c -- plain CPU oracle for the block-scale fp8 GEMM hot path of a
+ * row-parallel linear layer (DeepSeek wo_b), its destination-major band
+ * layout, the local fp32 band reduce and the per-row e4m3 "fp8 wire" codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may load this
+ * library: only the test suite, the smoke check and the benchmark's
+ * cpu_baseline leg do.  It shares no code, header, table or constant
+ * generator with the HIP kernels; the two meet only on the seeded inputs.
+ *
+ * Pages this follows (cited by title and section):
+ *   [PR40757]   sglang PR 40757, "[AMD][gfx950] DSV4: fuse wo_b's GEMM with
+ *               its all-reduce via mori cco" -- sections "What", "Numbers",
+ *               "The optional fp8 gather, and what it costs".
+ *   [PR43480]   sglang PR 43480 (the V4.1-Flash successor) -- "What",
+ *               "Numerics, measured where the path engages".
+ *   [MORI]      "MORI GEMM + All-Reduce Benchmark" -- "Running the
+ *               benchmark" (--quant blockscale), "Where the time goes",
+ *               "The fp8 wire", "What fp8 costs, numerically",
+ *               "Negative results".
+ *
+ * Arithmetic policy: doubles wherever a step is claimed exact, IEEE binary32
+ * (round to nearest even) wherever the method computes in fp32, explicit
+ * fmaf() where a fused multiply-add is part of the definition.  Build with
+ * -O2 -ffp-contract=off and without fast-math so the compiler adds no
+ * contraction or reassociation.  OpenMP only splits independent outputs
+ * across threads; no output's arithmetic is reordered.
+ *
+ * Every function returns 0 on success and a negative value when an input is
+ * outside its domain (non-finite data, bad sizes).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_E4M3_MAX 448.0
+
+/* ------------------------------------------------------------------ O1 --
+ * e4m3 decode.  The wire and operand format is OCP FP8 E4M3 ("fn"): 1 sign
+ * bit, 4 exponent bits with bias 7, 3 mantissa bits, no infinities, NaN only
+ * at S.1111.111, largest finite 448.  [MORI] "The fp8 wire" names e4m3 and its
+ * 3 mantissa bits; [PR43480] takes 448 as the top of the e4m3 grid; the target
+ * is gfx950, whose fp8 is the OCP variant (max 448), not the older FNUZ one.
+ *   exponent field 0     : (-1)^s * m * 2^-9           (subnormal)
+ *   exponent field 1..15 : (-1)^s * (8 + m) * 2^(e-10)  (except e=15,m=7)
+ */
+double orc_e4m3_value(int code) {
+    int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = (double)m * ldexp(1.0, -9);
+    else
+        v = (double)(8 + m) * ldexp(1.0, e - 10);
+    return s ? -v : v;
+}
+
+/* magnitude of code k for k = 0..126, strictly increasing in k */
+static double mag_of(int k) { return orc_e4m3_value(k); }
+
+/* ------------------------------------------------------------------ O2 --
+ * e4m3 encode: the nearest e4m3 value to v, ties to the even code (mantissa
+ * LSB 0), magnitudes above 448 saturate to 448, sign kept (so -0 and any
+ * negative value that rounds to zero give 0x80).  Nearest-value search over
+ * the 127 finite non-negative magnitudes, done in double (exact for every
+ * fp32 v).  Non-finite v is outside the domain: returns -1.
+ */
+int orc_e4m3_code(float v) {
+    int sign = signbit(v) ? 0x80 : 0;
+    double a = fabs((double)v);
+    int lo, hi;
+    if (isnan(v) || isinf(v)) return -1;
+    if (a >= ORC_E4M3_MAX) return 0x7E | sign;
+    /* largest k with mag(k) <= a; mag(0) = 0 <= a always */
+    lo = 0;
+    hi = 126;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (mag_of(mid) <= a) lo = mid; else hi = mid - 1;
+    }
+    {
+        int k = lo;
+        double dlo = a - mag_of(k), dhi = mag_of(k + 1) - a;
+        if (dhi < dlo || (dhi == dlo && (k & 1))) k = k + 1;
+        return k | sign;
+    }
+}
+
+/* O2 over an array (codes for n fp32 values); -1 if any value is non-finite */
+int orc_e4m3_code_array(const float *v, int64_t n, uint8_t *out) {
+    int64_t i;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (i = 0; i < n; i++) {
+        int c = orc_e4m3_code(v[i]);
+        if (c < 0) { bad = 1; c = 0; }
+        out[i] = (uint8_t)c;
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------- bf16 ------
+ * bf16 is the upper half of a binary32.  Widening is exact; narrowing is
+ * round-to-nearest-even: of the two bf16 neighbours of x pick the nearer,
+ * on a tie the one with an even last mantissa bit.  The neighbour above the
+ * largest finite bf16 is 2^128 for the comparison and becomes infinity.
+ * NaN gives the quiet NaN 0x7FC0 with x's sign.
+ */
+float orc_bf16_value(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t orc_bf16_rne(float x) {
+    uint32_t u, sign;
+    double a, vlo, vhi;
+    uint16_t lo;
+    memcpy(&u, &x, 4);
+    sign = u & 0x80000000u;
+    if (isnan(x)) return (uint16_t)((sign >> 16) | 0x7FC0);
+    if (isinf(x)) return (uint16_t)(u >> 16);
+    a = fabs((double)x);
+    lo = (uint16_t)((u & 0x7FFFFFFFu) >> 16);          /* truncation: |lo| <= a */
+    vlo = (double)orc_bf16_value(lo);
+    vhi = (lo == 0x7F7F) ? ldexp(1.0, 128) : (double)orc_bf16_value((uint16_t)(lo + 1));
+    if (vhi - a < a - vlo || (vhi - a == a - vlo && (lo & 1))) lo = (uint16_t)(lo + 1);
+    return (uint16_t)(lo | (sign >> 16));
+}
+
+/* bf16 narrowing over an array */
+int orc_bf16_rne_array(const float *x, int64_t n, uint16_t *out) {
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; i++) out[i] = orc_bf16_rne(x[i]);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ O3 --
+ * Block quantizer (operand preparation).  [MORI] "Running the benchmark":
+ * --quant blockscale quantises A per 1x128 block and B per 128x128 block with
+ * fp32 scales.  Per block: amax = max |x|; s = amax / 448 in fp32; each code
+ * is the e4m3 encoding of the fp32 quotient x / s.  A block whose scale is 0
+ * (all zeros, or amax so small that amax/448 underflows) stores s = 0 and
+ * all codes 0x00.  x is [rows, cols] row-major; q the same; s is
+ * [ceil(rows/br), ceil(cols/bc)] row-major.
+ */
+int orc_quant_blocks(const float *x, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                     uint8_t *q, float *s) {
+    int64_t nbr, nbc, bi;
+    int bad = 0;
+    if (rows < 0 || cols < 0 || br <= 0 || bc <= 0) return -2;
+    nbr = (rows + br - 1) / br;
+    nbc = (cols + bc - 1) / bc;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+    for (bi = 0; bi < nbr * nbc; bi++) {
+        int64_t r0 = (bi / nbc) * br, c0 = (bi % nbc) * bc, r, c;
+        int64_t r1 = r0 + br < rows ? r0 + br : rows, c1 = c0 + bc < cols ? c0 + bc : cols;
+        float amax = 0.0f, sc;
+        for (r = r0; r < r1; r++)
+            for (c = c0; c < c1; c++) {
+                float v = x[r * cols + c];
+                if (!isfinite(v)) bad = 1;
+                if (fabsf(v) > amax) amax = fabsf(v);
+            }
+        sc = amax / 448.0f;
+        s[bi] = sc;
+        for (r = r0; r < r1; r++)
+            for (c = c0; c < c1; c++) {
+                int code = 0;
+                if (sc != 0.0f) code = orc_e4m3_code(x[r * cols + c] / sc);
+                if (code < 0) { bad = 1; code = 0; }
+                q[r * cols + c] = (uint8_t)code;
+            }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ O4 --
+ * Block-scale GEMM element.  C = A * B^T with A [M,K] e4m3 + sa [M,K/128],
+ * B [N,K] e4m3 + sb [N/128,K/128] ([PR40757] "What": wo_b is a block-scale
+ * fp8 GEMM; [MORI] "Running the benchmark": A 1x128, B 128x128, fp32
+ * scales; [MORI] "Negative results": one 16x16x128 MFMA per 128-deep K
+ * block).  For each K block kb in ascending order:
+ *   p   = sum over the block's 128 k of dec(a) * dec(b)  (exact in double:
+ *         every product is a multiple of 2^-18 and |sum| < 2^25), then
+ *         rounded once to fp32;
+ *   s   = sa[m,kb] * sb[n/128,kb]                        (fp32);
+ *   acc = fmaf(p, s, acc)                                 (fp32, from 0).
+ * The output is bf16_rne(acc).  The MFMA's own internal summation order is
+ * hardware-defined, which is why device results are compared at a relL2
+ * tolerance rather than bitwise ([PR40757] "Numbers": what separates two
+ * correct paths is accumulation order).
+ */
+static double g_dec[256];
+static int g_dec_ready = 0;
+
+static void dec_init(void) {
+    int c;
+    if (g_dec_ready) return;
+    for (c = 0; c < 256; c++) g_dec[c] = orc_e4m3_value(c);
+    g_dec_ready = 1;
+}
+
+static float gemm_elem(const uint8_t *qa, const float *sa, const uint8_t *qb, const float *sb,
+                       int64_t K, int64_t m, int64_t n) {
+    int64_t KB = K / 128, kb, k;
+    float acc = 0.0f;
+    for (kb = 0; kb < KB; kb++) {
+        double dot = 0.0;
+        float p, s;
+        for (k = kb * 128; k < kb * 128 + 128; k++)
+            dot += g_dec[qa[m * K + k]] * g_dec[qb[n * K + k]];
+        p = (float)dot;
+        s = sa[m * KB + kb] * sb[(n / 128) * KB + kb];
+        acc = fmaf(p, s, acc);
+    }
+    return acc;
+}
+
+static int gemm_args_ok(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0 || K % 128 || N % 128) return 0;
+    dec_init();
+    return 1;
+}
+
+/* full product: acc [M,N] fp32 (may be NULL) and c [M,N] bf16 row-major */
+int orc_bsgemm(const uint8_t *qa, const float *sa, const uint8_t *qb, const float *sb,
+               int64_t M, int64_t N, int64_t K, float *acc, uint16_t *c) {
+    int64_t m;
+    if (!gemm_args_ok(M, N, K)) return -2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (m = 0; m < M; m++) {
+        int64_t n;
+        for (n = 0; n < N; n++) {
+            float v = gemm_elem(qa, sa, qb, sb, K, m, n);
+            if (acc) acc[m * N + n] = v;
+            if (c) c[m * N + n] = orc_bf16_rne(v);
+        }
+    }
+    return 0;
+}
+
+/* sampled elements (mi[i], ni[i]) for i < count, for full-size checks */
+int orc_bsgemm_elems(const uint8_t *qa, const float *sa, const uint8_t *qb, const float *sb,
+                     int64_t M, int64_t N, int64_t K, const int64_t *mi, const int64_t *ni,
+                     int64_t count, float *acc, uint16_t *c) {
+    int64_t i;
+    int bad = 0;
+    if (!gemm_args_ok(M, N, K)) return -2;
+#pragma omp parallel for schedule(dynamic, 64) reduction(| : bad)
+    for (i = 0; i < count; i++) {
+        float v;
+        if (mi[i] < 0 || mi[i] >= M || ni[i] < 0 || ni[i] >= N) { bad = 1; continue; }
+        v = gemm_elem(qa, sa, qb, sb, K, mi[i], ni[i]);
+        if (acc) acc[i] = v;
+        if (c) c[i] = orc_bf16_rne(v);
+    }
+    return bad ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------ O5 --
+ * Destination-major band layout.  [PR40757] "What": the GEMM writes each
+ * destination's row band as its own unit.  With band_rows = M / bands, row m
+ * belongs to band d = m / band_rows at row r = m % band_rows, stored at
+ * element d*band_stride + r*N + n.  Elements of out outside the bands are not
+ * touched.  c is the row-major [M,N] product.
+ */
+int orc_band_store(const uint16_t *c, int64_t M, int64_t N, int64_t bands, int64_t band_stride,
+                   uint16_t *out) {
+    int64_t band_rows, m, n;
+    if (bands <= 0 || M % bands || N <= 0) return -2;
+    band_rows = M / bands;
+    if (band_stride < band_rows * N) return -2;
+    for (m = 0; m < M; m++) {
+        int64_t d = m / band_rows, r = m % band_rows;
+        for (n = 0; n < N; n++) out[d * band_stride + r * N + n] = c[m * N + n];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ O6 --
+ * Band reduce.  [MORI] "Where the time goes" (row reduce) and "The fp8 wire":
+ * the reduce accumulates in fp32 and its output is bf16; "Negative results":
+ * one pass streams all P source slices.  Per element: acc = 0.0f, then
+ * acc += widen(part_p) for p = 0..P-1 in index order (fp32 adds), output
+ * bf16_rne(acc).
+ */
+int orc_band_reduce(const uint16_t *const *parts, int P, int64_t rows, int64_t N, uint16_t *out) {
+    int64_t i, total;
+    if (P < 1 || rows < 0 || N < 0) return -2;
+    total = rows * N;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < total; i++) {
+        float acc = 0.0f;
+        int p;
+        for (p = 0; p < P; p++) acc = acc + orc_bf16_value(parts[p][i]);
+        out[i] = orc_bf16_rne(acc);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ O7 --
+ * Per-row e4m3 quantize (the fp8 wire).  [MORI] "The fp8 wire": e4m3 with
+ * one fp32 scale per row; "What fp8 costs, numerically": per row is the
+ * granularity chosen.  Per row: amax = max |x| (exact); s = amax / 448 in
+ * fp32; q = e4m3 encoding of the fp32 quotient x / s.  A zero scale (zero
+ * row, or amax/448 underflowing) stores s = 0 and all codes 0x00.
+ * x bf16 [rows,N]; q u8 [rows,N]; s fp32 [rows].
+ */
+int orc_rowq(const uint16_t *x, int64_t rows, int64_t N, uint8_t *q, float *s) {
+    int64_t r;
+    int bad = 0;
+    if (rows < 0 || N <= 0) return -2;
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : bad)
+    for (r = 0; r < rows; r++) {
+        float amax = 0.0f, sc;
+        int64_t n;
+        for (n = 0; n < N; n++) {
+            float v = orc_bf16_value(x[r * N + n]);
+            if (!isfinite(v)) bad = 1;
+            if (fabsf(v) > amax) amax = fabsf(v);
+        }
+        sc = amax / 448.0f;
+        s[r] = sc;
+        for (n = 0; n < N; n++) {
+            int code = 0;
+            if (sc != 0.0f) code = orc_e4m3_code(orc_bf16_value(x[r * N + n]) / sc);
+            if (code < 0) { bad = 1; code = 0; }
+            q[r * N + n] = (uint8_t)code;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ O8 --
+ * Per-row e4m3 dequantize ("widen" after the gather, [MORI] "Where the time
+ * goes" row dequantize, "Who moves the gather").  y = bf16_rne(fp32(dec(q)) *
+ * s_row): the decode is exact in fp32, the product is one fp32 multiply, the
+ * narrowing is bf16 round-to-nearest-even.  NaN codes are outside the
+ * codec's range (the quantizer never emits them) and are not given a meaning.
+ */
+int orc_rowdq(const uint8_t *q, const float *s, int64_t rows, int64_t N, uint16_t *y) {
+    int64_t r;
+    if (rows < 0 || N <= 0) return -2;
+    dec_init();
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; r++) {
+        int64_t n;
+        for (n = 0; n < N; n++) {
+            float v = (float)g_dec[q[r * N + n]] * s[r];
+            y[r * N + n] = orc_bf16_rne(v);
+        }
+    }
+    return 0;
+}
+
+/* threads an OpenMP region will use (for reporting the baseline's cores) */
+int orc_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,168 @@
+"""Pins for the oracle's block-scale GEMM (O4), block quantizer (O3) and band
+layout (O5).
+
+The GEMM is checked against a different formulation of the same product --
+dequantize both operands (code value times its block's scale) and multiply in
+float64 with numpy -- under a rounding bound derived from the fp32 steps the
+definition takes, against the unquantized fp32 product (which pins the
+orientation C = A * B^T and the multiply-by-scale semantics), and against
+exact special cases (unit scales, powers of two, zero rows, permutations).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+T = None
+
+
+def table():
+    global T
+    if T is None:
+        T = oracle.e4m3_table()
+    return T
+
+
+def dequant_a(qa, sa):
+    return table()[qa] * np.repeat(sa.astype(np.float64), 128, axis=1)
+
+
+def dequant_b(qb, sb):
+    return table()[qb] * np.kron(sb.astype(np.float64), np.ones((128, 128)))
+
+
+def block_abs_sum(qa, sa, qb, sb):
+    """sum over K blocks of |p_kb * s_kb| (float64), the scale of the fp32 error"""
+    t = table()
+    M, K = qa.shape
+    N = qb.shape[0]
+    E = np.zeros((M, N))
+    for kb in range(K // 128):
+        ks = slice(kb * 128, kb * 128 + 128)
+        P = t[qa[:, ks]] @ t[qb[:, ks]].T
+        S = sa[:, kb].astype(np.float64)[:, None] * np.repeat(sb[:, kb].astype(np.float64), 128)[None, :]
+        E += np.abs(P * S)
+    return E
+
+
+def bf16_midpoint_distance(D):
+    """distance from each float64 value to the nearest bf16 rounding midpoint"""
+    a = np.abs(D)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    ulp = 2.0 ** (np.maximum(e, -126) - 7)
+    f = a / ulp
+    return np.abs(f - np.floor(f) - 0.5) * ulp
+
+
+def quantized(M, N, K, seed=0, heavy=False):
+    A, B = synth.operand_fp32(M, N, K, seed=seed, heavy=heavy)
+    qa, sa = oracle.quant_blocks(A, 1, 128)
+    qb, sb = oracle.quant_blocks(B, 128, 128)
+    return A, B, qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("shape,heavy", [((256, 512, 256), False), ((384, 256, 512), True)])
+def test_gemm_vs_dequantized_matmul(shape, heavy):
+    M, N, K = shape
+    A, B, qa, sa, qb, sb = quantized(M, N, K, seed=0, heavy=heavy)
+    acc, c = oracle.bsgemm(qa, sa, qb, sb)
+    D = dequant_a(qa, sa) @ dequant_b(qb, sb).T
+    E = block_abs_sum(qa, sa, qb, sb)
+    bound = (K // 128 + 2) * 2.0 ** -24 * E + 1e-30
+    err = np.abs(acc.astype(np.float64) - D)
+    assert np.all(err <= bound), float(np.max(err / bound))
+    # bf16 output equals bf16(D) except where D sits within the bound of a midpoint
+    cD = oracle.bf16_rne_array(D.astype(np.float32))
+    diff = c != cD
+    assert np.all(bf16_midpoint_distance(D)[diff] <= bound[diff] + np.abs(D[diff]) * 2.0 ** -24)
+    assert diff.mean() < 1e-3
+
+
+def test_gemm_is_a_times_b_transposed():
+    """The quantized product tracks the unquantized fp32 A @ B^T to the fp8
+    error level (about 2.6% per operand), and not any other orientation."""
+    A, B, qa, sa, qb, sb = quantized(256, 512, 256, seed=0)
+    acc, _ = oracle.bsgemm(qa, sa, qb, sb)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    r = oracle.rel_l2(acc, ref)
+    assert 0.01 < r < 0.05, r
+
+
+def test_block_quantizer_dequantizes_close():
+    A, B, qa, sa, qb, sb = quantized(256, 512, 256, seed=0)
+    # every nonzero block holds a +-448 code; error at most half a grid step
+    Ad = dequant_a(qa, sa)
+    for m in range(0, 256, 37):
+        for kb in range(2):
+            blk = qa[m, kb * 128:(kb + 1) * 128]
+            assert np.any((blk == 0x7E) | (blk == 0xFE))
+    rel = np.abs(Ad - A) / np.repeat(sa.astype(np.float64), 128, axis=1)
+    assert np.max(rel) <= 16.0 + 1e-9  # half of the widest step (32 at 256..448), in units of s
+    assert oracle.rel_l2(Ad, A) < 0.03
+    assert sb.shape == (4, 2) and sa.shape == (256, 2)
+
+
+def test_gemm_unit_scales_exact():
+    """With unit scales the method is a plain fp8 matmul; with codes whose
+    values are small multiples of 1/2 every partial sum is exact in fp32, so
+    the result equals the float64 matmul of the decoded values exactly."""
+    rng = np.random.default_rng(1)
+    t = table()
+    small = np.array([c for c in range(256) if np.isfinite(t[c]) and abs(t[c]) <= 8 and (t[c] * 2) % 1 == 0])
+    M, N, K = 64, 256, 512
+    qa = rng.choice(small, size=(M, K)).astype(np.uint8)
+    qb = rng.choice(small, size=(N, K)).astype(np.uint8)
+    sa = np.ones((M, K // 128), np.float32)
+    sb = np.ones((N // 128, K // 128), np.float32)
+    acc, c = oracle.bsgemm(qa, sa, qb, sb)
+    ref = t[qa] @ t[qb].T
+    assert np.array_equal(acc.astype(np.float64), ref)
+
+
+def test_gemm_power_of_two_scale_invariance():
+    A, B, qa, sa, qb, sb = quantized(128, 256, 384, seed=3)
+    acc, c = oracle.bsgemm(qa, sa, qb, sb)
+    acc2, c2 = oracle.bsgemm(qa, sa * np.float32(8.0), qb, sb * np.float32(0.5))
+    assert np.array_equal(acc2, acc * np.float32(4.0))
+
+
+def test_gemm_zero_rows_and_permutation():
+    A, B, qa, sa, qb, sb = quantized(256, 256, 256, seed=4)
+    qa[10] = 0
+    sa[20] = 0
+    acc, c = oracle.bsgemm(qa, sa, qb, sb)
+    assert np.all(acc[10] == 0) and np.all(c[10] == 0)
+    assert np.all(acc[20] == 0) and np.all(c[20] == 0)
+    perm = np.random.default_rng(5).permutation(256)
+    acc_p, c_p = oracle.bsgemm(qa[perm], sa[perm], qb, sb)
+    assert np.array_equal(acc_p, acc[perm]) and np.array_equal(c_p, c[perm])
+
+
+def test_gemm_sampled_elements_match_full():
+    A, B, qa, sa, qb, sb = quantized(256, 512, 256, seed=0)
+    acc, c = oracle.bsgemm(qa, sa, qb, sb)
+    mi, ni = synth.sample_indices(256, 512, 500)
+    acc_s, c_s = oracle.bsgemm_elems(qa, sa, qb, sb, mi, ni)
+    assert np.array_equal(acc_s, acc[mi, ni]) and np.array_equal(c_s, c[mi, ni])
+
+
+@pytest.mark.parametrize("M,bands", [(256, 8), (20096, 8), (384, 3)])
+def test_band_store_layout(M, bands):
+    N = 256
+    rng = np.random.default_rng(M)
+    c = rng.integers(0, 65536, size=(M, N), dtype=np.uint64).astype(np.uint16)
+    band_rows = M // bands
+    # contiguous stride: byte-identical to row-major
+    out = np.zeros(M * N, np.uint16)
+    oracle.band_store(c, bands, band_rows * N, out)
+    assert np.array_equal(out, c.reshape(-1))
+    # padded stride: each band in its own slot, gaps untouched
+    stride = band_rows * N + 96
+    out = np.full(bands * stride, 0xDEAD, np.uint16)
+    oracle.band_store(c, bands, stride, out)
+    for d in range(bands):
+        blk = out[d * stride: d * stride + band_rows * N].reshape(band_rows, N)
+        assert np.array_equal(blk, c[d * band_rows:(d + 1) * band_rows])
+        assert np.all(out[d * stride + band_rows * N:(d + 1) * stride] == 0xDEAD)
