@@ -1,0 +1,274 @@
+"""Benchmark of the per-GPU wo_b step on one MI355X.
+
+One step = the whole hot path over one batch: block-scale fp8 GEMM
+(M=16384, N=7168, K=2048) written as 8 destination-major bands, the fp32
+reduce of the own band with 7 stand-in partial bands, per-row e4m3 quantize
+of the reduced band, and dequantize of the [16384, 7168] wire buffer.
+
+Prints ONE JSON line.  `value` is whole-step throughput expressed in GEMM
+TFLOP/s (2*M*N*K per step / step time); `phases` gives each kernel's own
+average time and rate inside the timed steps; `roofline` is the GEMM's
+(measured with HIP events on the launch stream); `streaming` gives the
+HBM-bound kernels measured alone on rotating buffers (>1 GiB, so the 256 MB
+Infinity Cache cannot serve repeats); `cpu_baseline` is the CPU oracle timed
+on a bounded row sample of the same workload and projected to a full step.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "blockscale fp8 GEMM TFLOP/s @16384x7168x2048 (% MFMA peak); reduce/quant GB/s"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+PAGES_STEP_US = 438.2 + 42.5 + 11.8 + 61.0   # gemm+reduce+quantize+dequantize, fp8/sdma column
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_chunk16k_traffic.json")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "codec.hpp"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_bsgemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per GEMM launch from the committed counter runs, if they were
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_hash") != kernel_hash():
+        return None
+    return t.get("traffic_bytes")
+
+
+def build_inputs(M, N, K, P, dev):
+    import numpy as np
+    import torch
+    import block_scaled_fp8_bsgemm_amd as bs
+    import synth
+
+    A, B = synth.operand_fp32(M, N, K, seed=0, heavy=True)
+    dA32 = torch.from_numpy(A).to(dev)
+    dB32 = torch.from_numpy(B).to(dev)
+    qa, sa = bs.blockq_e4m3(dA32, 1)
+    qb, sb = bs.blockq_e4m3(dB32, 128)
+    del dA32, dB32
+    band_rows = M // P
+    parts = [torch.from_numpy(p.view(np.int16)).to(dev).view(torch.bfloat16)
+             for p in synth.partial_bands(band_rows, N, P=P, seed0=100)[1:]]
+    wire = torch.from_numpy(synth.wire_rows(M, N, seed=200).view(np.int16)).to(dev).view(torch.bfloat16)
+    wq, ws = bs.rowq_e4m3(wire)
+    del wire
+    torch.cuda.synchronize()
+    return qa, sa, qb, sb, parts, wq, ws
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step.step()
+    torch.cuda.synchronize()
+    ev = {ph: [] for ph in step.PHASES}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        for ph in step.PHASES:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            getattr(step, ph)()
+            e1.record()
+            ev[ph].append((e0, e1))
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    phase_ms = {ph: sum(a.elapsed_time(b) for a, b in ev[ph]) / steps for ph in step.PHASES}
+    return total_ms / steps, phase_ms, wall
+
+
+def streaming_rates(M, N, P, dev, iters=20):
+    """band_reduce / rowq / rowdq alone, rotating over buffer sets of > 1 GiB."""
+    import torch
+    import block_scaled_fp8_bsgemm_amd as bs
+    band_rows = M // P
+    out = {}
+
+    def timed(fn, nsets):
+        for i in range(nsets):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            fn(i % nsets)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e-3
+
+    # reduce: 8 x [2048,7168] bf16 in, one out: 264 MB per call; 5 sets
+    nset = 5
+    red_in = [[torch.randn(band_rows, N, device=dev).to(torch.bfloat16) for _ in range(P)] for _ in range(nset)]
+    red_out = [torch.empty(band_rows, N, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
+    t = timed(lambda i: bs.band_reduce(red_in[i], red_out[i]), nset)
+    b = (P + 1) * band_rows * N * 2
+    out["band_reduce"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    # rowq: [2048,7168] bf16 -> u8 + scales: 44 MB per call; 24 sets
+    nset = 24
+    rq_in = [red_out[i % len(red_out)] if i < len(red_out) else torch.randn(band_rows, N, device=dev).to(torch.bfloat16)
+             for i in range(nset)]
+    rq_q = [torch.empty(band_rows, N, dtype=torch.uint8, device=dev) for _ in range(nset)]
+    rq_s = [torch.empty(band_rows, dtype=torch.float32, device=dev) for _ in range(nset)]
+    del red_in
+    t = timed(lambda i: bs.rowq_e4m3(rq_in[i], rq_q[i], rq_s[i]), nset)
+    b = band_rows * N * 3 + band_rows * 4
+    out["rowq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    # rowdq: [16384,7168] u8 -> bf16: 352 MB per call; 4 sets
+    nset = 4
+    dq_q = [torch.randint(0, 0x7E, (M, N), dtype=torch.uint8, device=dev) for _ in range(nset)]
+    dq_s = [torch.rand(M, device=dev) for _ in range(nset)]
+    dq_y = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
+    del rq_in, rq_q, rq_s
+    t = timed(lambda i: bs.rowdq_e4m3(dq_q[i], dq_s[i], dq_y[i]), nset)
+    b = M * N * 3 + M * 4
+    out["rowdq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    del dq_q, dq_s, dq_y
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(M, N, K, P, target_s=8.0):
+    """The oracle (test infrastructure, not tuned) on a bounded sample of the
+    same workload: the GEMM on the first R rows (R doubled until one call
+    takes >= target_s or R = 256), the reduce and quantize on the full band and
+    the dequantize on 2048 rows; projected to one full step."""
+    import numpy as np
+    import oracle
+    import synth
+
+    A, B = synth.operand_fp32(M, N, K, seed=0, heavy=True)
+    qb, sb = oracle.quant_blocks(B, 128, 128)
+    R = 16
+    while True:
+        qa, sa = oracle.quant_blocks(A[:R], 1, 128)
+        t0 = time.perf_counter()
+        oracle.bsgemm(qa, sa, qb, sb)
+        tg = time.perf_counter() - t0
+        if tg >= target_s or R >= 256:
+            break
+        R *= 2
+    band_rows = M // P
+    parts = synth.partial_bands(band_rows, N, P=P, seed0=100)
+    t0 = time.perf_counter()
+    red = oracle.band_reduce(parts)
+    tr = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.rowq(red)
+    tq = time.perf_counter() - t0
+    wq, ws = oracle.rowq(synth.wire_rows(band_rows, N, seed=200))
+    t0 = time.perf_counter()
+    oracle.rowdq(wq, ws)
+    td = (time.perf_counter() - t0) * (M / band_rows)
+    step_s = tg * (M / R) + tr + tq + td
+    flops = 2.0 * M * N * K
+    return {"value": flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"GEMM on the first {R} of {M} rows ({tg:.2f} s, scaled x{M // R}); reduce and quantize "
+                      f"of one full [{band_rows},{N}] band ({tr:.2f} s, {tq:.2f} s); dequantize of "
+                      f"{band_rows} rows scaled x{M // band_rows} ({td:.2f} s projected)",
+            "projected_step_s": step_s}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streaming", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the collectives between ranks are out of scope); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_scaled_fp8_bsgemm_amd as bs
+    from block_scaled_fp8_bsgemm_amd.pipeline import WoBStep
+
+    bs.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, N, K, P = 16384, 7168, 2048, 8
+    print(f"[bench] building inputs M={M} N={N} K={K} P={P}", file=sys.stderr, flush=True)
+    qa, sa, qb, sb, parts, wq, ws = build_inputs(M, N, K, P, dev)
+    step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P)
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    ms, phase_ms, wall = time_steps(step, args.steps, args.warmup)
+
+    flops = 2.0 * M * N * K
+    band_rows = M // P
+    gemm_s = phase_ms["gemm"] * 1e-3
+    gemm_tflops = flops / gemm_s / 1e12
+    bytes_of = {
+        "reduce": P * band_rows * N * 2 + band_rows * N * 2,
+        "quantize": band_rows * N * 2 + band_rows * N + band_rows * 4,
+        "dequantize": M * N + M * 4 + M * N * 2,
+    }
+    phases = {"gemm": {"us": phase_ms["gemm"] * 1e3, "TFLOP/s": gemm_tflops,
+                       "frac_fp8_peak": gemm_tflops / PEAK_FP8_TFLOPS}}
+    for ph in ("reduce", "quantize", "dequantize"):
+        t = phase_ms[ph] * 1e-3
+        phases[ph] = {"us": t * 1e6, "bytes": bytes_of[ph], "GB/s": bytes_of[ph] / t / 1e9}
+    traffic = load_traffic()
+    value = flops / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": value / (flops / (PAGES_STEP_US * 1e-6) / 1e12),
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "wo_b per-GPU step (blockscale fp8 GEMM + 8-band epilogue, band reduce P=8, "
+                               "row e4m3 quantize, dequantize)",
+                   "M": M, "N": N, "K": K, "P": P, "bands": P},
+        "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gemm_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,
+                     "kernel": "bsgemm_tile_kernel", "algorithmic_flop_per_launch": flops},
+        "phases": phases,
+        "wall_s_timed": wall,
+    }
+    if not args.no_streaming:
+        print("[bench] streaming kernels alone (rotating buffers)", file=sys.stderr, flush=True)
+        del step, parts, wq, ws
+        torch.cuda.empty_cache()
+        rec["streaming"] = streaming_rates(M, N, P, dev)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu_baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(M, N, K, P)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,179 @@
+"""MI355X (gfx950) hot path of a row-parallel block-scale fp8 linear layer.
+
+Thin ctypes binding over ``libbsgemm.so`` (declared in ``include/bsgemm.h``):
+the functions here only check and marshal torch tensors (device pointers,
+sizes, the current HIP stream) and raise on a non-OK status.  Every step of
+the path runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, importing the functions raises immediately.
+
+  bsgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0)
+  band_reduce(parts, out=None)
+  rowq_e4m3(x, q=None, scale=None)
+  rowdq_e4m3(q, scale, y=None)
+  blockq_e4m3(x, block_rows, q=None, scale=None)
+
+Tensors: e4m3 codes are uint8 (or torch.float8_e4m3fn, reinterpreted), bf16
+values are torch.bfloat16 (or int16/uint16 bit patterns), scales float32.
+All tensors must live on the current CUDA (HIP) device and be contiguous.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbsgemm.so")
+
+BS_OK, BS_ERR_INVALID, BS_ERR_UNSUPPORTED, BS_ERR_LAUNCH = 0, 1, 2, 3
+
+# every extern "C" symbol of include/bsgemm.h
+EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "bs_status_str")
+
+_lib = None
+
+
+class BSError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} (status {status})")
+
+
+def load():
+    """Load libbsgemm.so (built in-tree by ``_build.py``); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m block_scaled_fp8_bsgemm_amd._build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    L.bsgemm_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp]
+    L.band_reduce.argtypes = [ctypes.POINTER(vp), i32, vp, i64, i64, vp]
+    L.rowq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
+    L.rowdq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
+    L.blockq_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3"):
+        getattr(L, f).restype = ctypes.c_int
+    L.bs_status_str.argtypes = [ctypes.c_int]
+    L.bs_status_str.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_str(status):
+    return load().bs_status_str(int(status)).decode()
+
+
+def _check(status, what):
+    if status != BS_OK:
+        raise BSError(status, what)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtypes, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _u8():
+    torch = _torch()
+    return (torch.uint8, torch.int8, torch.float8_e4m3fn)
+
+
+def _b16():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _f32():
+    return (_torch().float32,)
+
+
+def bsgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0, stream=None):
+    """C (bf16) = blockscale(A [M,K] e4m3, a_scale [M,K/128]) x blockscale(B [N,K], b_scale [N/128,K/128])^T,
+    written as `bands` destination-major row bands (band d at element d*band_stride)."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        band_rows = M // bands if bands > 0 else 0
+        stride = band_stride if band_stride else band_rows * N
+        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+    st = load().bsgemm_fp8(_ptr(A, _u8(), "A"), _ptr(a_scale, _f32(), "a_scale"),
+                           _ptr(B, _u8(), "B"), _ptr(b_scale, _f32(), "b_scale"),
+                           _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
+    _check(st, "bsgemm_fp8")
+    return C
+
+
+def band_reduce(parts, out=None, stream=None):
+    """out (bf16 [rows,N]) = bf16(sum_p fp32(parts[p])), parts summed in index order."""
+    torch = _torch()
+    parts = list(parts)
+    rows, N = parts[0].shape
+    if out is None:
+        out = torch.empty((rows, N), dtype=torch.bfloat16, device=parts[0].device)
+    ptrs = (ctypes.c_void_p * len(parts))(*[_ptr(p, _b16(), "part") for p in parts])
+    for p in parts:
+        if tuple(p.shape) != (rows, N):
+            raise ValueError("all parts must have the same shape")
+    st = load().band_reduce(ptrs, len(parts), _ptr(out, _b16(), "out"), rows, N, _stream(stream))
+    _check(st, "band_reduce")
+    return out
+
+
+def rowq_e4m3(x, q=None, scale=None, stream=None):
+    """(q uint8 [rows,N], scale fp32 [rows]) = per-row e4m3 quantization of bf16 x."""
+    torch = _torch()
+    rows, N = x.shape
+    if q is None:
+        q = torch.empty((rows, N), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    st = load().rowq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
+                          rows, N, _stream(stream))
+    _check(st, "rowq_e4m3")
+    return q, scale
+
+
+def rowdq_e4m3(q, scale, y=None, stream=None):
+    """y (bf16 [rows,N]) = bf16(decode(q) * scale[row])."""
+    torch = _torch()
+    rows, N = q.shape
+    if y is None:
+        y = torch.empty((rows, N), dtype=torch.bfloat16, device=q.device)
+    st = load().rowdq_e4m3(_ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"), _ptr(y, _b16(), "y"),
+                           rows, N, _stream(stream))
+    _check(st, "rowdq_e4m3")
+    return y
+
+
+def blockq_e4m3(x, block_rows, q=None, scale=None, stream=None):
+    """(q uint8 [rows,cols], scale fp32 [ceil(rows/block_rows), cols/128]) for fp32 x."""
+    torch = _torch()
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(((rows + block_rows - 1) // block_rows, cols // 128), dtype=torch.float32,
+                            device=x.device)
+    st = load().blockq_e4m3(_ptr(x, _f32(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
+                            rows, cols, block_rows, _stream(stream))
+    _check(st, "blockq_e4m3")
+    return q, scale

@@ -1,0 +1,291 @@
+// gemm.hip -- block-scale fp8 GEMM with a destination-major band epilogue
+// for gfx950 (MI355X).
+//
+// Computes C = A * B^T for A [M,K] e4m3 with one fp32 scale per 1x128 block
+// and B [N,K] e4m3 with one fp32 scale per 128x128 block, accumulating in
+// fp32 and writing bf16 ("MORI GEMM + All-Reduce Benchmark", "Running the
+// benchmark", --quant blockscale; sglang PR 40757, "What").  Each 128-deep K
+// block of a 16x16 output sub-tile is one v_mfma_f32_16x16x128_f8f6f4 into a
+// zeroed fp32 temporary; its result is folded into the running accumulator
+// with one fma by the block's combined scale a_scale[m,kb] * b_scale[n/128,kb],
+// K blocks in ascending order.  The epilogue writes each output row straight
+// into its destination's row band (sglang PR 40757, "What": the GEMM writes
+// each destination's row band as its own unit).
+//
+// Tiling (one workgroup = 8 waves = 512 lanes, one 256x256 output tile):
+//  - per K block the A tile [256 x 128 B] and B tile [256 x 128 B] are staged
+//    in LDS, double buffered (2 x 64 KiB); 16-byte chunks are XOR-swizzled by
+//    row so the MFMA operand reads hit distinct banks;
+//  - global loads use buffer descriptors sized to the matrix, so rows past M
+//    (a ragged last tile) read as zero without any branch;
+//  - waves form a 2 (M) x 4 (N) grid of 128 x 64 wave tiles (8 x 4 MFMA
+//    sub-tiles, 128 fp32 accumulator registers per lane);
+//  - the MFMA takes the B fragment as its first operand, so each lane ends up
+//    holding 4 consecutive output columns of one output row: one combined
+//    scale per lane per sub-tile row, and 8-byte stores in the epilogue;
+//  - the combined scales a_scale * b_scale for the tile's 256 rows and its two
+//    128-column b_scale blocks are formed once per K block by the loader
+//    lanes and kept in LDS next to the operands;
+//  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
+//    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
+//    in groups of 8 M-tiles so that concurrently running tiles share A and B
+//    panels in that XCD's L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int NTHREADS = 512;
+constexpr int WM = 128, WN = 64;        // wave tile
+constexpr int TM = WM / 16, TN = WN / 16;
+constexpr int GROUP_M = 8;
+constexpr int NUM_XCD = 8;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+struct GemmArgs {
+    const uint8_t *A;
+    const float *sa;
+    const uint8_t *B;
+    const float *sb;
+    uint16_t *C;
+    int64_t M, N, K;
+    int64_t band_rows, band_stride;
+    int KB;                 // K / 128
+    int NB;                 // N / 128
+    int tiles_m, tiles_n;
+};
+
+// The two pipeline stages are distinct LDS objects so that the compiler can
+// tell a DMA into one stage from reads of the other and does not serialise
+// them with a wait.
+__shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * BK];
+__shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * BK];
+__shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * BK];
+__shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * BK];
+// scales per stage: [0, 256) a_scale of the tile's rows; [256, 512) four 64-entry
+// slots filled by waves 4..7 with b_scale, of which entries 256 and 257 (the
+// tile's two 128-column blocks) are read
+constexpr int SCALES = BM + 256;
+__shared__ __attribute__((aligned(1024))) float sS0[SCALES];
+__shared__ __attribute__((aligned(1024))) float sS1[SCALES];
+
+template <int ST> __device__ __forceinline__ uint8_t *stA() { return ST ? sA1 : sA0; }
+template <int ST> __device__ __forceinline__ uint8_t *stB() { return ST ? sB1 : sB0; }
+template <int ST> __device__ __forceinline__ float *stS() { return ST ? sS1 : sS0; }
+
+
+// byte offset of 16-byte chunk `c` (0..7) of tile row `r` inside a staged
+// [rows x 128 B] operand tile: chunks are XOR-swizzled by the row's low bits
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    int32_t n = bytes > 0x7FFFFFFFll ? 0x7FFFFFFF : (bytes > 0 ? (int32_t)bytes : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+}
+
+struct Loader {
+    __amdgpu_buffer_rsrc_t rA, rB, rS;   // rS: a_scale (waves 0..3) or b_scale (4..7)
+    int voff;    // this lane's byte offset of its chunk in the A / B row panels
+    int k8;      // 8 rows of a panel, in bytes
+    int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
+    int ldsq;    // byte offset of this wave's first 1 KiB LDS slot
+    int sdst;    // byte offset of this wave's 256-byte scale slot (waves 0..4)
+};
+
+// DMA the K block kb of the A and B panels and of the A scales into stage ST.
+// One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
+// lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
+// logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
+template <int ST>
+__device__ __forceinline__ void load_stage(const Loader &L, int kb) {
+    const int koff = kb * BK;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int q = L.ldsq + i * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rA, (lds_void *)(stA<ST>() + q), 16,
+                                                 L.voff + i * L.k8, koff, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rB, (lds_void *)(stB<ST>() + q), 16,
+                                                 L.voff + i * L.k8, koff, 0, 0);
+    }
+    // waves 0..3: a_scale of rows 64w..64w+63; waves 4..7: b_scale of the
+    // column blocks from the tile's first one on (each wave its own slot).
+    // No branch: every wave issues exactly one.
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rS, (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
+                                             L.soff, kb * 4, 0, 0);
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t *st, int r, int fc) {
+    const u32x4 lo = *(const u32x4 *)(st + swz(r, fc));
+    const u32x4 hi = *(const u32x4 *)(st + swz(r, fc + 1));
+    return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+__device__ __forceinline__ void fold4(v4f &acc, const v4f &p, float s) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc[e] = __builtin_fmaf(p[e], s, acc[e]);
+}
+
+// One K block from stage ST: 8 x 4 MFMAs per wave.  Software pipelined one
+// MFMA deep: the 4 results of MFMA k are folded into the accumulators while
+// MFMA k+1 executes, so only two 4-register temporaries are live.
+template <int ST>
+__device__ __forceinline__ void compute_stage(v4f (&acc)[TM][TN], int wm, int wn, int frow, int fc) {
+    const uint8_t *a = stA<ST>();
+    const uint8_t *b = stB<ST>();
+    const float *sc = stS<ST>();
+    // this wave's 64 columns lie inside one 128-column b_scale block
+    const float sbv = sc[BM + (wn >> 1)];   // wave 4's slot: entries BM, BM+1
+    v8i bf[TN];
+#pragma unroll
+    for (int j = 0; j < TN; j++) bf[j] = lds_frag(b, wn * WN + j * 16 + frow, fc);
+    float s[TM];
+#pragma unroll
+    for (int i = 0; i < TM; i++) s[i] = sc[wm * WM + i * 16 + frow] * sbv;
+
+    // MFMA k's result is folded three MFMAs later, when it is certainly
+    // ready, so no wait states are needed and only 4 temporaries are live;
+    // the hard scheduling barriers keep the compiler from hoisting MFMAs.
+    constexpr int D = 3;
+    v4f p[D + 1];
+    v8i an = lds_frag(a, wm * WM + frow, fc);
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const v8i af = an;
+        if (i + 1 < TM) an = lds_frag(a, wm * WM + (i + 1) * 16 + frow, fc);
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int k = i * TN + j;
+            p[k % (D + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bf[j], af, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            if (k >= D) {
+                const int kp = k - D;
+                fold4(acc[kp / TN][kp % TN], p[kp % (D + 1)], s[kp / TN]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int kp = TM * TN - D; kp < TM * TN; kp++) fold4(acc[kp / TN][kp % TN], p[kp % (D + 1)], s[kp / TN]);
+}
+
+__device__ __forceinline__ void wait_dma_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(NTHREADS)
+bsgemm_tile_kernel(GemmArgs g) {
+    // ---- workgroup -> tile (XCD-aware, grouped) ----
+    const int T = g.tiles_m * g.tiles_n;
+    const int per_xcd = (T + NUM_XCD - 1) / NUM_XCD;
+    const int b = blockIdx.x;
+    const int t = (b % NUM_XCD) * per_xcd + b / NUM_XCD;
+    if (t >= T) return;
+    const int group = t / (GROUP_M * g.tiles_n);
+    const int first_m = group * GROUP_M;
+    const int gm = min(GROUP_M, g.tiles_m - first_m);
+    const int local = t - group * GROUP_M * g.tiles_n;
+    const int tm = first_m + local % gm;
+    const int tn = local / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+    const int wm = wave >> 2, wn = wave & 3;
+    const int64_t K = g.K;
+
+    // ---- operand descriptors: this tile's row panels, zero past the end ----
+    Loader L;
+    L.rA = make_rsrc(g.A + m0 * K, (g.M - m0) * K);
+    L.rB = make_rsrc(g.B + n0 * K, (g.N - n0) * K);
+    const int nb0 = (int)(n0 / 128);
+    L.rS = wave < 4 ? make_rsrc(g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
+                    : make_rsrc(g.sb + (int64_t)nb0 * g.KB, (int64_t)(g.NB - nb0) * g.KB * 4);
+    L.ldsq = wave * 4096;
+    {
+        const int row = wave * 32 + (lane >> 3);   // + 8 per slot i
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        L.voff = row * (int)K + chunk * 16;
+        L.k8 = 8 * (int)K;
+        L.soff = ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
+        L.sdst = wave * 256;
+    }
+
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int fc = (lane >> 4) * 2;
+
+    load_stage<0>(L, 0);
+    wait_dma_and_sync();
+    // K blocks in pairs: stage 0 holds even blocks, stage 1 odd ones; the
+    // next block is DMA'd into the idle stage while the other is consumed.
+    // The last one or two blocks are peeled so the loop body is straight-line.
+    int kb = 0;
+    for (; kb + 2 < g.KB; kb += 2) {
+        load_stage<1>(L, kb + 1);
+        compute_stage<0>(acc, wm, wn, frow, fc);
+        wait_dma_and_sync();
+        load_stage<0>(L, kb + 2);
+        compute_stage<1>(acc, wm, wn, frow, fc);
+        wait_dma_and_sync();
+    }
+    if (kb + 1 < g.KB) {
+        load_stage<1>(L, kb + 1);
+        compute_stage<0>(acc, wm, wn, frow, fc);
+        wait_dma_and_sync();
+        compute_stage<1>(acc, wm, wn, frow, fc);
+    } else {
+        compute_stage<0>(acc, wm, wn, frow, fc);
+    }
+
+    // ---- epilogue: lane holds C[m][n .. n+3], m = row of the A sub-tile ----
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const int64_t m = m0 + wm * WM + i * 16 + frow;
+        if (m >= g.M) continue;
+        const int64_t d = m / g.band_rows;
+        uint16_t *crow = g.C + d * g.band_stride + (m - d * g.band_rows) * g.N;
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int64_t n = n0 + wn * WN + j * 16 + (lane >> 4) * 4;
+            if (n >= g.N) continue;
+            uint2 w;
+            w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+            w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+            *(uint2 *)(crow + n) = w;
+        }
+    }
+}
+
+}  // namespace
+
+int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb,
+                   uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                   int64_t band_stride, hipStream_t stream) {
+    GemmArgs g;
+    g.A = A; g.sa = sa; g.B = B; g.sb = sb; g.C = C;
+    g.M = M; g.N = N; g.K = K;
+    g.band_rows = band_rows; g.band_stride = band_stride;
+    g.KB = (int)(K / 128);
+    g.NB = (int)(N / 128);
+    g.tiles_m = (int)((M + BM - 1) / BM);
+    g.tiles_n = (int)((N + BN - 1) / BN);
+    const int T = g.tiles_m * g.tiles_n;
+    const int grid = ((T + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
+    return bs_enqueue(bsgemm_tile_kernel, dim3(grid), dim3(NTHREADS), stream, g);
+}

@@ -1,0 +1,396 @@
+// stream.hip -- the HBM-bound kernels of the wo_b hot path (gfx950):
+//
+//   band_reduce  fp32 sum of P bf16 partial bands -> bf16 band
+//                ("MORI GEMM + All-Reduce Benchmark", "Where the time goes",
+//                row reduce; "The fp8 wire": fp32 accumulation, bf16 output;
+//                "Negative results": a flat grid over 16-byte packs, each
+//                pack streamed through all P source slices at once)
+//   rowq_e4m3    per-row e4m3 quantize, one fp32 scale per row ("The fp8
+//                wire"; "Negative results": the row amax forces a row-wide
+//                reduction, so the quantizer is its own kernel)
+//   rowdq_e4m3   per-row dequantize to bf16 ("Where the time goes",
+//                dequantize; "Who moves the gather")
+//   blockq_e4m3  fp32 operand -> e4m3 + fp32 scale per 1x128 or 128x128 block
+//                (the blockscale operand format of "Running the benchmark")
+//
+// All of them move 16-byte vectors with coalesced, unit-stride accesses and
+// keep each lane's data in registers between the load and the store.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.hpp"
+#include "launch.hpp"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ band reduce --
+
+struct PartPtrs {
+    const u32x4 *p[16];
+};
+
+// one 16-byte pack (8 bf16) of every part per lane and iteration; the P loads
+// are issued together before the fp32 adds, which run in part order from +0.
+template <int P>
+__global__ void __launch_bounds__(256)
+band_reduce_kernel(PartPtrs parts, u32x4 *__restrict__ out, int64_t nvec) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+        u32x4 w[P];
+#pragma unroll
+        for (int p = 0; p < P; p++) w[p] = __builtin_nontemporal_load(parts.p[p] + v);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[e] = 0.0f;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                acc[2 * e] += bf16_lo(w[p][e]);
+                acc[2 * e + 1] += bf16_hi(w[p][e]);
+            }
+        }
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+        out[v] = o;
+    }
+}
+
+template <int P>
+int launch_reduce_p(const PartPtrs &pp, u32x4 *out, int64_t nvec, hipStream_t stream) {
+    int rc = 0;
+    int64_t blocks = (nvec + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    rc |= bs_enqueue(band_reduce_kernel<P>, dim3((unsigned)blocks), dim3(256), stream, pp,
+                       out, nvec);
+    return rc;
+}
+
+// ----------------------------------------------------------- row quantize --
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// 8 bf16 (one 16-byte pack) -> 8 e4m3 codes with per-row reciprocal R
+__device__ __forceinline__ u32x2 quant_pack(u32x4 w, double R) {
+    u32x2 o;
+    o[0] = pack_e4m3x4(wire_quotient(bf16_lo(w[0]), R), wire_quotient(bf16_hi(w[0]), R),
+                      wire_quotient(bf16_lo(w[1]), R), wire_quotient(bf16_hi(w[1]), R));
+    o[1] = pack_e4m3x4(wire_quotient(bf16_lo(w[2]), R), wire_quotient(bf16_hi(w[2]), R),
+                      wire_quotient(bf16_lo(w[3]), R), wire_quotient(bf16_hi(w[3]), R));
+    return o;
+}
+
+__device__ __forceinline__ float pack_absmax(u32x4 w) {
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+    return m;
+}
+
+// One 256-lane workgroup per row; each lane keeps up to CPT packs of the row
+// in registers across the amax reduction (row length N <= 2048 * CPT).
+template <int CPT>
+__global__ void __launch_bounds__(256)
+rowq_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scale,
+            int64_t rows, int nch) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const u32x4 *xr = x + row * nch;
+        u32x4 v[CPT];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int c = tid + 256 * i;
+            if (c < nch) {
+                v[i] = xr[c];
+                amax = fmaxf(amax, pack_absmax(v[i]));
+            }
+        }
+        amax = wave_max(amax);
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();  // red[] is rewritten by the next row
+        const float s = amax / 448.0f;
+        if (tid == 0) scale[row] = s;
+        u32x2 *qr = q + row * nch;
+        if (s == 0.0f) {
+#pragma unroll
+            for (int i = 0; i < CPT; i++) {
+                const int c = tid + 256 * i;
+                if (c < nch) qr[c] = (u32x2){0u, 0u};
+            }
+            continue;
+        }
+        const double R = 1.0 / (double)s;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int c = tid + 256 * i;
+            if (c < nch) qr[c] = quant_pack(v[i], R);
+        }
+    }
+}
+
+// Rows longer than the register-resident variant: amax pass, then a second
+// pass that re-reads the row (from L2) and encodes it.
+__global__ void __launch_bounds__(256)
+rowq_long_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scale,
+                 int64_t rows, int nch) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const u32x4 *xr = x + row * nch;
+        float amax = 0.0f;
+        for (int c = tid; c < nch; c += 256) amax = fmaxf(amax, pack_absmax(xr[c]));
+        amax = wave_max(amax);
+        if (lane == 0) red[wave] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        const float s = amax / 448.0f;
+        if (tid == 0) scale[row] = s;
+        u32x2 *qr = q + row * nch;
+        if (s == 0.0f) {
+            for (int c = tid; c < nch; c += 256) qr[c] = (u32x2){0u, 0u};
+            continue;
+        }
+        const double R = 1.0 / (double)s;
+        for (int c = tid; c < nch; c += 256) qr[c] = quant_pack(xr[c], R);
+    }
+}
+
+// --------------------------------------------------------- row dequantize --
+
+// 8 codes -> 8 bf16: exact decode, one fp32 multiply, round to nearest even
+__device__ __forceinline__ u32x4 dequant_pack(u32x2 c, float s) {
+    const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[0], false);
+    const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[0], true);
+    const v2f d = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[1], false);
+    const v2f e = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[1], true);
+    u32x4 o;
+    o[0] = pack_bf16x2(a[0] * s, a[1] * s);
+    o[1] = pack_bf16x2(b[0] * s, b[1] * s);
+    o[2] = pack_bf16x2(d[0] * s, d[1] * s);
+    o[3] = pack_bf16x2(e[0] * s, e[1] * s);
+    return o;
+}
+
+// one 128-lane workgroup per row, UPT packs of 8 codes per lane, all loads
+// issued before the first store
+template <int UPT>
+__global__ void __launch_bounds__(128)
+rowdq_kernel(const u32x2 *__restrict__ q, const float *__restrict__ scale, u32x4 *__restrict__ y,
+             int64_t rows, int nch) {
+    const int tid = threadIdx.x;
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float s = scale[row];
+        const u32x2 *qr = q + row * nch;
+        u32x4 *yr = y + row * nch;
+        u32x2 v[UPT];
+#pragma unroll
+        for (int i = 0; i < UPT; i++) {
+            const int c = tid + 128 * i;
+            if (c < nch) v[i] = __builtin_nontemporal_load(qr + c);
+        }
+#pragma unroll
+        for (int i = 0; i < UPT; i++) {
+            const int c = tid + 128 * i;
+            if (c < nch) yr[c] = dequant_pack(v[i], s);
+        }
+    }
+}
+
+__global__ void __launch_bounds__(128)
+rowdq_long_kernel(const u32x2 *__restrict__ q, const float *__restrict__ scale,
+                  u32x4 *__restrict__ y, int64_t rows, int nch) {
+    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+        const float s = scale[row];
+        for (int c = threadIdx.x; c < nch; c += 128) y[row * nch + c] = dequant_pack(q[row * nch + c], s);
+    }
+}
+
+// -------------------------------------------------------- block quantizer --
+
+__device__ __forceinline__ float pack_absmax_f32(u32x4 w) {
+    return fmaxf(fmaxf(fabsf(__uint_as_float(w[0])), fabsf(__uint_as_float(w[1]))),
+                 fmaxf(fabsf(__uint_as_float(w[2])), fabsf(__uint_as_float(w[3]))));
+}
+
+__device__ __forceinline__ uint32_t quant4_f32(u32x4 w, double R) {
+    return pack_e4m3x4(wire_quotient(__uint_as_float(w[0]), R), wire_quotient(__uint_as_float(w[1]), R),
+                       wire_quotient(__uint_as_float(w[2]), R), wire_quotient(__uint_as_float(w[3]), R));
+}
+
+// 1x128 blocks: 16 lanes per block, 8 consecutive fp32 per lane.  Blocks are
+// contiguous in a row-major [rows, cols] matrix with cols % 128 == 0, so the
+// flat block index is also the index into the [rows, cols/128] scale array.
+__global__ void __launch_bounds__(256)
+blockq_1x128_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scale,
+                    int64_t nblocks) {
+    const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t blk = gt >> 4;
+    const bool live = blk < nblocks;
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (live) {
+        a = x[gt * 2];
+        b = x[gt * 2 + 1];
+    }
+    float amax = fmaxf(pack_absmax_f32(a), pack_absmax_f32(b));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (!live) return;
+    const float s = amax / 448.0f;
+    if ((threadIdx.x & 15) == 0) scale[blk] = s;
+    u32x2 o = (u32x2){0u, 0u};
+    if (s != 0.0f) {
+        const double R = 1.0 / (double)s;
+        o[0] = quant4_f32(a, R);
+        o[1] = quant4_f32(b, R);
+    }
+    q[gt] = o;
+}
+
+// 128x128 blocks: one 256-lane workgroup per block; lane t covers row t/2 of
+// the block and 64 consecutive columns.
+__global__ void __launch_bounds__(256)
+blockq_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q,
+                      float *__restrict__ scale, int64_t rows, int64_t cols) {
+    __shared__ float red[4];
+    const int64_t nbc = cols / 128;
+    const int64_t br = blockIdx.x / nbc, bc = blockIdx.x % nbc;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t r = br * 128 + (tid >> 1);
+    const int64_t c0 = bc * 128 + (tid & 1) * 64;
+    const bool live = r < rows;
+    u32x4 v[16];
+    float amax = 0.0f;
+    const u32x4 *xr = (const u32x4 *)(x + r * cols + c0);
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        v[i] = live ? xr[i] : (u32x4){0u, 0u, 0u, 0u};
+        amax = fmaxf(amax, pack_absmax_f32(v[i]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax / 448.0f;
+    if (tid == 0) scale[blockIdx.x] = s;
+    if (!live) return;
+    u32x4 *qr = (u32x4 *)(q + r * cols + c0);
+    const double R = s != 0.0f ? 1.0 / (double)s : 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        u32x4 o = {0u, 0u, 0u, 0u};
+        if (s != 0.0f) {
+            o[0] = quant4_f32(v[4 * i + 0], R);
+            o[1] = quant4_f32(v[4 * i + 1], R);
+            o[2] = quant4_f32(v[4 * i + 2], R);
+            o[3] = quant4_f32(v[4 * i + 3], R);
+        }
+        qr[i] = o;
+    }
+}
+
+unsigned grid_rows(int64_t rows) { return (unsigned)(rows < 1048576 ? (rows > 0 ? rows : 1) : 1048576); }
+
+}  // namespace
+
+int bs_launch_band_reduce(const uint16_t *const *parts, int P, uint16_t *out, int64_t rows,
+                          int64_t N, hipStream_t stream) {
+    int rc = 0;
+    PartPtrs pp;
+    for (int p = 0; p < 16; p++) pp.p[p] = (const u32x4 *)parts[p < P ? p : 0];
+    const int64_t nvec = rows * N / 8;
+    u32x4 *o = (u32x4 *)out;
+    switch (P) {
+        case 1: rc = launch_reduce_p<1>(pp, o, nvec, stream); break;
+        case 2: rc = launch_reduce_p<2>(pp, o, nvec, stream); break;
+        case 3: rc = launch_reduce_p<3>(pp, o, nvec, stream); break;
+        case 4: rc = launch_reduce_p<4>(pp, o, nvec, stream); break;
+        case 5: rc = launch_reduce_p<5>(pp, o, nvec, stream); break;
+        case 6: rc = launch_reduce_p<6>(pp, o, nvec, stream); break;
+        case 7: rc = launch_reduce_p<7>(pp, o, nvec, stream); break;
+        case 8: rc = launch_reduce_p<8>(pp, o, nvec, stream); break;
+        case 9: rc = launch_reduce_p<9>(pp, o, nvec, stream); break;
+        case 10: rc = launch_reduce_p<10>(pp, o, nvec, stream); break;
+        case 11: rc = launch_reduce_p<11>(pp, o, nvec, stream); break;
+        case 12: rc = launch_reduce_p<12>(pp, o, nvec, stream); break;
+        case 13: rc = launch_reduce_p<13>(pp, o, nvec, stream); break;
+        case 14: rc = launch_reduce_p<14>(pp, o, nvec, stream); break;
+        case 15: rc = launch_reduce_p<15>(pp, o, nvec, stream); break;
+        case 16: rc = launch_reduce_p<16>(pp, o, nvec, stream); break;
+        default: return -1;
+    }
+    return rc;
+}
+
+int bs_launch_rowq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t N,
+                   hipStream_t stream) {
+    int rc = 0;
+    const int nch = (int)(N / 8);
+    const dim3 grid(grid_rows(rows)), block(256);
+    const u32x4 *xv = (const u32x4 *)x;
+    u32x2 *qv = (u32x2 *)q;
+    if (nch <= 256)
+        rc |= bs_enqueue(rowq_kernel<1>, grid, block, stream, xv, qv, scale, rows, nch);
+    else if (nch <= 512)
+        rc |= bs_enqueue(rowq_kernel<2>, grid, block, stream, xv, qv, scale, rows, nch);
+    else if (nch <= 1024)
+        rc |= bs_enqueue(rowq_kernel<4>, grid, block, stream, xv, qv, scale, rows, nch);
+    else if (nch <= 2048)
+        rc |= bs_enqueue(rowq_kernel<8>, grid, block, stream, xv, qv, scale, rows, nch);
+    else
+        rc |= bs_enqueue(rowq_long_kernel, grid, block, stream, xv, qv, scale, rows, nch);
+    return rc;
+}
+
+int bs_launch_rowdq(const uint8_t *q, const float *scale, uint16_t *y, int64_t rows, int64_t N,
+                    hipStream_t stream) {
+    int rc = 0;
+    const int nch = (int)(N / 8);
+    const dim3 grid(grid_rows(rows)), block(128);
+    const u32x2 *qv = (const u32x2 *)q;
+    u32x4 *yv = (u32x4 *)y;
+    if (nch <= 128)
+        rc |= bs_enqueue(rowdq_kernel<1>, grid, block, stream, qv, scale, yv, rows, nch);
+    else if (nch <= 256)
+        rc |= bs_enqueue(rowdq_kernel<2>, grid, block, stream, qv, scale, yv, rows, nch);
+    else if (nch <= 512)
+        rc |= bs_enqueue(rowdq_kernel<4>, grid, block, stream, qv, scale, yv, rows, nch);
+    else if (nch <= 1024)
+        rc |= bs_enqueue(rowdq_kernel<8>, grid, block, stream, qv, scale, yv, rows, nch);
+    else
+        rc |= bs_enqueue(rowdq_long_kernel, grid, block, stream, qv, scale, yv, rows, nch);
+    return rc;
+}
+
+int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
+                     int block_rows, hipStream_t stream) {
+    int rc = 0;
+    if (block_rows == 1) {
+        const int64_t nblocks = rows * (cols / 128);
+        const int64_t threads = nblocks * 16;
+        const int64_t wg = (threads + 255) / 256;
+        if (wg > 0x7FFFFFFF) return -1;
+        hipLaunchKernelGGL(blockq_1x128_kernel, dim3((unsigned)(wg > 0 ? wg : 1)), dim3(256), 0, stream,
+                           (const u32x4 *)x, (u32x2 *)q, scale, nblocks);
+    } else {
+        const int64_t nb = ((rows + 127) / 128) * (cols / 128);
+        if (nb > 0x7FFFFFFF) return -1;
+        hipLaunchKernelGGL(blockq_128x128_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(256), 0, stream,
+                           x, q, scale, rows, cols);
+    }
+    return rc;
+}

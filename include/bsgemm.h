@@ -1,0 +1,177 @@
+/*
+ * bsgemm.h -- C ABI of libbsgemm, the MI355X (gfx950) hot path of a
+ * row-parallel block-scale fp8 linear layer (DeepSeek-V4-Pro's wo_b):
+ *
+ *   bsgemm_fp8   block-scale fp8 GEMM, fp32 accumulate, bf16 out, written as
+ *                destination-major row bands
+ *   band_reduce  fp32 sum of P bf16 partial bands into one bf16 band
+ *   rowq_e4m3    per-row e4m3 quantize with one fp32 scale per row
+ *   rowdq_e4m3   per-row e4m3 dequantize back to bf16
+ *   blockq_e4m3  fp32 operand -> e4m3 codes + fp32 block scales (the
+ *                activation/weight quantizer that produces bsgemm_fp8's input)
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [PR40757] sglang PR 40757 "[AMD][gfx950] DSV4: fuse wo_b's GEMM with its
+ *             all-reduce via mori cco": "What" (block-scale fp8 GEMM followed
+ *             by an all-reduce of [M, hidden]; each destination's row band
+ *             written as its own unit), "Numbers" (fused and unfused agree up
+ *             to accumulation order).
+ *   [MORI]    "MORI GEMM + All-Reduce Benchmark": "Running the benchmark"
+ *             (--quant blockscale: A per 1x128, B per 128x128, fp32 scales;
+ *             shape [M,7168], K=2048), "Where the time goes" (reduce /
+ *             quantize / dequantize phases), "The fp8 wire" (e4m3 with one
+ *             fp32 scale per row; the reduce accumulates in fp32 and outputs
+ *             bf16), "Negative results" (reduce and quantize kept separate).
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are DEVICE memory owned by the caller (the library
+ *    never allocates, frees or keeps a pointer after returning).  The only
+ *    host memory argument is band_reduce's array of part pointers, read
+ *    before the call returns.
+ *  - bf16 values are passed as their uint16_t bit patterns; e4m3 values as
+ *    uint8_t codes of the OCP FP8 E4M3 ("fn") format (max 448, NaN at
+ *    S.1111.111, no infinities).  Every matrix is dense row-major.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    only enqueue work: they return before the device finishes and never
+ *    synchronize.
+ *  - Arguments are validated on the host before anything is enqueued.  On
+ *    BS_ERR_INVALID or BS_ERR_UNSUPPORTED nothing is launched and no output
+ *    byte is written.  BS_ERR_LAUNCH means the HIP runtime refused the launch
+ *    (hipGetLastError after the enqueue); outputs are then unspecified.
+ *  - Results are bitwise deterministic for identical inputs and shapes.
+ *  - The library holds no global state that calls depend on, reads no
+ *    environment variables and is safe to call from several host threads.
+ *    Calls whose output ranges overlap another call's input or output on a
+ *    concurrently running stream race, as with any kernel.
+ */
+#ifndef BSGEMM_H
+#define BSGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BS_OK = 0,
+    BS_ERR_INVALID = 1,     /* null pointer, negative size, aliasing outputs */
+    BS_ERR_UNSUPPORTED = 2, /* well-formed but not expressible by the kernels */
+    BS_ERR_LAUNCH = 3       /* the HIP runtime rejected the launch */
+} bs_status;
+
+/*
+ * Block-scale fp8 GEMM with a destination-major band epilogue.
+ * [PR40757] "What"; [MORI] "Running the benchmark" (--quant blockscale).
+ *
+ *   C[m, n] = bf16_rne( acc[m, n] ),  acc accumulated in fp32 over the K
+ *   blocks kb = 0 .. K/128-1 in ascending order:
+ *     acc += ( sum_{k in block kb} A[m,k] * B[n,k] ) * (a_scale[m,kb] * b_scale[n/128,kb])
+ *   the block dot product being one 16x16x128 fp8 MFMA with fp32 result.
+ *
+ *   A        [M, K]          e4m3 codes (activations)
+ *   a_scale  [M, K/128]      fp32, one scale per 1x128 block of A
+ *   B        [N, K]          e4m3 codes (the weight as stored, [out, in])
+ *   b_scale  [N/128, K/128]  fp32, one scale per 128x128 block of B
+ *   C        bf16 output as `bands` row bands of band_rows = M / bands rows:
+ *            row m lives in band d = m / band_rows at row r = m % band_rows,
+ *            element (m, n) at C[d * band_stride + r * N + n].
+ *            band_stride = 0 means band_rows * N (contiguous: identical to a
+ *            row-major [M, N] matrix).  Elements between bands are untouched.
+ *
+ * Requirements: M >= 0 (M = 0 is a no-op); N > 0 and N % 128 == 0;
+ * K > 0 and K % 128 == 0; 1 <= bands <= 64 and M % bands == 0;
+ * band_stride == 0 or band_stride >= band_rows * N; A, B and C 16-byte
+ * aligned, a_scale and b_scale 4-byte aligned; C must not overlap any input.
+ * Violations: null pointers, negative sizes, bands < 1 or overlap ->
+ * BS_ERR_INVALID; the rest -> BS_ERR_UNSUPPORTED.  M need not be a multiple
+ * of the tile: ragged rows are handled in the kernel.
+ */
+bs_status bsgemm_fp8(const uint8_t *A, const float *a_scale,
+                     const uint8_t *B, const float *b_scale,
+                     uint16_t *C,
+                     int64_t M, int64_t N, int64_t K,
+                     int32_t bands, int64_t band_stride,
+                     void *stream);
+
+/*
+ * Band reduce: out = bf16_rne( sum_{p=0..P-1} widen(parts[p]) ), the sum in
+ * fp32 starting from +0.0 and taken in part-index order.
+ * [MORI] "Where the time goes" (reduce), "The fp8 wire" (fp32 accumulate,
+ * bf16 output), "Negative results" (one pass streams all P source slices).
+ *
+ *   parts  HOST array of P device pointers, each a bf16 [rows, N] band
+ *   out    bf16 [rows, N]; may not overlap any part
+ *
+ * Requirements: 1 <= P <= 16; rows >= 0, N > 0, N % 8 == 0; every pointer
+ * 16-byte aligned.  Null or out-of-range P -> BS_ERR_INVALID; N % 8 or
+ * misalignment -> BS_ERR_UNSUPPORTED.
+ */
+bs_status band_reduce(const uint16_t *const *parts, int32_t P,
+                      uint16_t *out, int64_t rows, int64_t N,
+                      void *stream);
+
+/*
+ * Per-row e4m3 quantize (the "fp8 wire").  [MORI] "The fp8 wire" (e4m3 with
+ * one fp32 scale per row), "What fp8 costs, numerically" (per row chosen).
+ *
+ *   for each row r:  amax = max_n |x[r,n]|;  scale[r] = amax / 448 (fp32,
+ *   round to nearest even);  q[r,n] = e4m3 code nearest to the fp32 quotient
+ *   x[r,n] / scale[r] (ties to even, |.| > 448 saturates, sign kept so a
+ *   negative value that rounds to zero gives 0x80).  A row whose scale is 0
+ *   (all zeros, or amax/448 underflowing) gets scale 0 and codes 0x00.
+ *
+ *   x      bf16 [rows, N] (finite values; non-finite input is outside the
+ *          contract and gives unspecified codes)
+ *   q      e4m3 [rows, N]
+ *   scale  fp32 [rows]
+ *
+ * Requirements: rows >= 0, N > 0, N % 8 == 0; x, q 16-byte aligned, scale
+ * 4-byte aligned; q and scale must not overlap x or each other.
+ */
+bs_status rowq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
+                    int64_t rows, int64_t N, void *stream);
+
+/*
+ * Per-row e4m3 dequantize ("widen" after the gather).  [MORI] "Where the
+ * time goes" (dequantize), "Who moves the gather".
+ *
+ *   y[r,n] = bf16_rne( fp32(decode(q[r,n])) * scale[r] )   (one fp32 multiply)
+ *
+ *   q      e4m3 [rows, N] (NaN codes 0x7F/0xFF are never produced by
+ *          rowq_e4m3 and are outside the contract)
+ *   scale  fp32 [rows]
+ *   y      bf16 [rows, N]
+ *
+ * Requirements: rows >= 0, N > 0, N % 8 == 0; q, y 16-byte aligned, scale
+ * 4-byte aligned; y must not overlap q or scale.
+ */
+bs_status rowdq_e4m3(const uint8_t *q, const float *scale, uint16_t *y,
+                     int64_t rows, int64_t N, void *stream);
+
+/*
+ * Block quantizer for GEMM operands.  [MORI] "Running the benchmark"
+ * (--quant blockscale: activations per 1x128 block, weights per 128x128
+ * block, fp32 scales).  For each block of block_rows x 128 elements:
+ * amax = max |x|; s = amax / 448 (fp32); codes = e4m3 of the fp32 quotient
+ * x / s exactly as rowq_e4m3 (zero scale -> codes 0x00).
+ *
+ *   x      fp32 [rows, cols] (finite)
+ *   q      e4m3 [rows, cols]
+ *   scale  fp32 [ceil(rows/block_rows), cols/128]
+ *
+ * Requirements: block_rows is 1 or 128; rows >= 0; cols > 0, cols % 128 ==
+ * 0; x, q 16-byte aligned; scale 4-byte aligned; no output overlaps x.
+ */
+bs_status blockq_e4m3(const float *x, uint8_t *q, float *scale,
+                      int64_t rows, int64_t cols, int32_t block_rows,
+                      void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *bs_status_str(bs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGEMM_H */

@@ -1,0 +1,152 @@
+"""GPU parity of band_reduce, rowq_e4m3, rowdq_e4m3 and blockq_e4m3 against
+the oracle (O6, O7, O8, O3).  All of these are bit-exact: the device takes
+the same fp32 decisions in the same order as the definition."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_bsgemm_amd as bs
+import oracle
+import synth
+from gpuutil import bf16_dev, bits16, device, poison_bf16, poison_u8, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ reduce --
+
+@pytest.mark.parametrize("rows,N,P", [(2048, 7168, 8), (37, 104, 3), (5, 8, 1), (64, 1024, 16), (130, 7168, 8)])
+def test_band_reduce_bitexact(rows, N, P):
+    say(f"band_reduce rows={rows} N={N} P={P}")
+    parts = synth.partial_bands(rows, N, P=P, seed0=100)
+    ref = oracle.band_reduce(parts)
+    out = poison_bf16(torch.empty((rows, N), dtype=torch.bfloat16, device=device()))
+    bs.band_reduce([bf16_dev(p) for p in parts], out)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(out), ref)
+
+
+def test_band_reduce_order_and_zero_sign():
+    one = oracle.bf16_rne(1.0)
+    big = oracle.bf16_rne(2.0 ** 25)
+    parts = [np.full((4, 64), v, np.uint16) for v in (big, one, big | 0x8000)]
+    negz = [np.full((4, 64), 0x8000, np.uint16)] * 2
+    say("band_reduce order / -0")
+    out = bs.band_reduce([bf16_dev(p) for p in parts])
+    out2 = bs.band_reduce([bf16_dev(p) for p in negz])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(out), oracle.band_reduce(parts))
+    assert np.all(bits16(out) == 0)
+    assert np.all(bits16(out2) == 0)
+
+
+# ---------------------------------------------------------------- row codec --
+
+def rowq_dev(x_bits):
+    rows, N = x_bits.shape
+    q = poison_u8(torch.empty((rows, N), dtype=torch.uint8, device=device()))
+    s = torch.full((rows,), float("nan"), dtype=torch.float32, device=device())
+    bs.rowq_e4m3(bf16_dev(x_bits), q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("rows,N", [(2048, 7168), (3, 8), (17, 2056), (2, 40960)])
+def test_rowq_bitexact(rows, N):
+    say(f"rowq_e4m3 rows={rows} N={N}")
+    x = synth.wire_rows(rows, N, seed=200)
+    qr, sr = oracle.rowq(x)
+    q, s = rowq_dev(x)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+
+
+def exhaustive_rows():
+    """Rows holding every finite bf16 value up to a chosen amax, for amax over
+    many binades (including amax whose scale amax/448 is an fp32 subnormal or
+    underflows to zero), plus zero, -0 and single-entry rows."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[(b & 0x7F80) != 0x7F80]
+    mag = b & 0x7FFF
+    amaxes = [0x0001, 0x0005, 0x0080, 0x0100, 0x2F55, 0x3F80, 0x3FC1, 0x4480, 0x43E0, 0x6000, 0x7F7F]
+    rows = []
+    width = b.size + 8
+    for a in amaxes:
+        sel = b[mag <= a]
+        row = np.zeros(width, np.uint16)
+        row[: sel.size] = sel
+        row[-1] = a
+        rows.append(row)
+    rows.append(np.zeros(width, np.uint16))
+    rows.append(np.full(width, 0x8000, np.uint16))
+    single = np.zeros(width, np.uint16)
+    single[123] = 0xC2F7
+    rows.append(single)
+    return np.stack(rows)
+
+
+def test_rowq_exhaustive_bf16():
+    x = exhaustive_rows()
+    say(f"rowq_e4m3 exhaustive {x.shape}")
+    qr, sr = oracle.rowq(x)
+    q, s = rowq_dev(x)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    bad = np.argwhere(q != qr)
+    assert bad.size == 0, [(int(r), int(c), hex(x[r, c]), hex(q[r, c]), hex(qr[r, c])) for r, c in bad[:8]]
+
+
+@pytest.mark.parametrize("rows,N", [(16384, 7168), (7, 24), (3, 33000)])
+def test_rowdq_bitexact(rows, N):
+    say(f"rowdq_e4m3 rows={rows} N={N}")
+    x = synth.wire_rows(rows, N, seed=200)
+    q, s = oracle.rowq(x)
+    ref = oracle.rowdq(q, s)
+    y = poison_bf16(torch.empty((rows, N), dtype=torch.bfloat16, device=device()))
+    bs.rowdq_e4m3(to_dev(q), to_dev(s), y)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(y), ref)
+
+
+def test_rowdq_every_code_and_scale():
+    t = oracle.e4m3_table()
+    codes = np.array([c for c in range(256) if np.isfinite(t[c])], np.uint8)
+    scales = np.array([1.0, 2.0 ** -9, 0.0091, 3.3e-4, 7.5e35, 1e-40, 0.0, 1.1754944e-38, 123.456], np.float32)
+    q = np.tile(np.resize(codes, 256), (scales.size, 1))
+    say("rowdq_e4m3 all codes x scales")
+    ref = oracle.rowdq(q, scales)
+    y = bs.rowdq_e4m3(to_dev(q), to_dev(scales))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(y), ref)
+
+
+def test_rowq_rowdq_roundtrip_exact_on_grid_rows():
+    """rows of e4m3 grid values times 2^e with a +-448 entry survive the round
+    trip bit for bit"""
+    rng = np.random.default_rng(11)
+    t = oracle.e4m3_table()
+    finite = np.array([c for c in range(256) if np.isfinite(t[c])])
+    codes = rng.choice(finite, size=(64, 512))
+    codes[np.arange(64), rng.integers(0, 512, 64)] = rng.choice([0x7E, 0xFE], size=64)
+    vals = t[codes] * (2.0 ** rng.integers(-20, 20, size=64))[:, None]
+    x = oracle.bf16_rne_array(vals.astype(np.float32))
+    say("rowq/rowdq grid round trip")
+    q, s = rowq_dev(x)
+    assert np.array_equal(q, codes.astype(np.uint8))
+    y = bs.rowdq_e4m3(to_dev(q), to_dev(s))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(y), x)
+
+
+# ---------------------------------------------------------- block quantizer --
+
+@pytest.mark.parametrize("rows,cols,br", [(256, 256, 1), (300, 640, 1), (4096, 2048, 1),
+                                          (256, 512, 128), (300, 384, 128), (7168, 2048, 128)])
+def test_blockq_bitexact(rows, cols, br):
+    say(f"blockq_e4m3 rows={rows} cols={cols} block_rows={br}")
+    x = synth.operand_fp32(rows, 128, cols, seed=5, heavy=True)[0]   # [rows, cols]
+    x[min(3, rows - 1), :128] = 0.0            # a zero block (1x128 case)
+    qr, sr = oracle.quant_blocks(x, br, 128)
+    q, s = bs.blockq_e4m3(to_dev(x), br)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qr)
