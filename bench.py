@@ -29,7 +29,7 @@ METRIC = "blockscale fp8 GEMM TFLOP/s @16384x7168x2048 (% MFMA peak); reduce/qua
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PAGES_STEP_US = 438.2 + 42.5 + 11.8 + 61.0   # gemm+reduce+quantize+dequantize, fp8/sdma column
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_chunk16k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsgemm_m16384_traffic.json")
 
 
 def kernel_hash():
@@ -153,26 +153,31 @@ def streaming_rates(M, N, P, dev, iters=20):
     return out
 
 
-def cpu_baseline(M, N, K, P, target_s=8.0):
+def cpu_baseline(M, N, K, P, target_s=10.0):
     """The oracle (test infrastructure, not tuned) on a bounded sample of the
-    same workload: the GEMM on the first R rows (R doubled until one call
-    takes >= target_s or R = 256), the reduce and quantize on the full band and
-    the dequantize on 2048 rows; projected to one full step."""
+    same workload: the GEMM on the first R rows (R doubled from 64 until one
+    call takes >= target_s or R = M), the reduce and quantize on the full band
+    and the dequantize on one band's rows; projected to one full step."""
     import numpy as np
     import oracle
     import synth
 
     A, B = synth.operand_fp32(M, N, K, seed=0, heavy=True)
     qb, sb = oracle.quant_blocks(B, 128, 128)
-    R = 16
-    while True:
+    def gemm_rows(R):
         qa, sa = oracle.quant_blocks(A[:R], 1, 128)
         t0 = time.perf_counter()
         oracle.bsgemm(qa, sa, qb, sb)
-        tg = time.perf_counter() - t0
-        if tg >= target_s or R >= 256:
-            break
-        R *= 2
+        t = time.perf_counter() - t0
+        print(f"[bench] cpu_baseline: oracle GEMM on {R} rows took {t:.2f} s", file=sys.stderr, flush=True)
+        return t
+
+    # a short probe sizes the timed sample to about target_s
+    R = 128
+    tg = gemm_rows(R)
+    if tg < target_s:
+        R = min(M, max(R, int(R * target_s / max(tg, 1e-3)) // 128 * 128))
+        tg = gemm_rows(R)
     band_rows = M // P
     parts = synth.partial_bands(band_rows, N, P=P, seed0=100)
     t0 = time.perf_counter()
@@ -188,7 +193,7 @@ def cpu_baseline(M, N, K, P, target_s=8.0):
     step_s = tg * (M / R) + tr + tq + td
     flops = 2.0 * M * N * K
     return {"value": flops / step_s / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"GEMM on the first {R} of {M} rows ({tg:.2f} s, scaled x{M // R}); reduce and quantize "
+            "sample": f"GEMM on the first {R} of {M} rows ({tg:.2f} s, scaled x{M / R:.2f}); reduce and quantize "
                       f"of one full [{band_rows},{N}] band ({tr:.2f} s, {tq:.2f} s); dequantize of "
                       f"{band_rows} rows scaled x{M // band_rows} ({td:.2f} s projected)",
             "projected_step_s": step_s}
@@ -201,6 +206,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streaming", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="after the steps, copy 1 GiB device-to-device once (a plain copy kernel of "
+                         "known size, for scaling the HBM byte counters of a profiler run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -259,6 +267,14 @@ def main():
         "phases": phases,
         "wall_s_timed": wall,
     }
+    if args.calib_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] calibration copy: 1073741824 B read, 1073741824 B written", file=sys.stderr, flush=True)
+        del src, dst
     if not args.no_streaming:
         print("[bench] streaming kernels alone (rotating buffers)", file=sys.stderr, flush=True)
         del step, parts, wq, ws
