@@ -93,6 +93,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 
 struct Loader {
     __amdgpu_buffer_rsrc_t rA, rB, rS;   // rS: a_scale (waves 0..3) or b_scale (4..7)
+    __amdgpu_buffer_rsrc_t rZ;           // zero-size: every load through it reads nothing
     int voff;    // this lane's byte offset of its chunk in the A / B row panels
     int k8;      // 8 rows of a panel, in bytes
     int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
@@ -104,21 +105,26 @@ struct Loader {
 // One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
 // lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
 // logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
+// A block past the end (valid == false) goes through the zero-size
+// descriptor: the loads touch no memory and the stage is not read again.
 template <int ST>
-__device__ __forceinline__ void load_stage(const Loader &L, int kb) {
+__device__ __forceinline__ void load_stage(const Loader &L, int kb, bool valid = true) {
     const int koff = kb * BK;
+    const __amdgpu_buffer_rsrc_t rA = valid ? L.rA : L.rZ;
+    const __amdgpu_buffer_rsrc_t rB = valid ? L.rB : L.rZ;
+    const __amdgpu_buffer_rsrc_t rS = valid ? L.rS : L.rZ;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int q = L.ldsq + i * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rA, (lds_void *)(stA<ST>() + q), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(stA<ST>() + q), 16,
                                                  L.voff + i * L.k8, koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rB, (lds_void *)(stB<ST>() + q), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(stB<ST>() + q), 16,
                                                  L.voff + i * L.k8, koff, 0, 0);
     }
     // waves 0..3: a_scale of rows 64w..64w+63; waves 4..7: b_scale of the
     // column blocks from the tile's first one on (each wave its own slot).
     // No branch: every wave issues exactly one.
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.rS, (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
                                              L.soff, kb * 4, 0, 0);
 }
 
@@ -134,52 +140,106 @@ __device__ __forceinline__ void fold4(v4f &acc, const v4f &p, float s) {
     for (int e = 0; e < 4; e++) acc[e] = __builtin_fmaf(p[e], s, acc[e]);
 }
 
-// One K block from stage ST: 8 x 4 MFMAs per wave.  Software pipelined one
-// MFMA deep: the 4 results of MFMA k are folded into the accumulators while
-// MFMA k+1 executes, so only two 4-register temporaries are live.
+__device__ __forceinline__ void wait_dma_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
+    __syncthreads();                     // ... and every other wave's; LDS reads are done
+}
+
+// The scales of one K block for this wave's rows: a_scale of its 8 row
+// groups (lane row m = 16 i + lane % 16 of the wave tile) and b_scale of its
+// column block; their products are the combined scales s[i].
+struct RawScales {
+    float sa[TM];
+    float sb;
+};
+
 template <int ST>
-__device__ __forceinline__ void compute_stage(v4f (&acc)[TM][TN], int wm, int wn, int frow, int fc) {
-    const uint8_t *a = stA<ST>();
-    const uint8_t *b = stB<ST>();
+__device__ __forceinline__ void read_scales(RawScales &r, int wm, int wn, int frow) {
     const float *sc = stS<ST>();
     // this wave's 64 columns lie inside one 128-column b_scale block
-    const float sbv = sc[BM + (wn >> 1)];   // wave 4's slot: entries BM, BM+1
-    v8i bf[TN];
+    r.sb = sc[BM + (wn >> 1)];   // wave 4's slot: entries BM, BM+1
 #pragma unroll
-    for (int j = 0; j < TN; j++) bf[j] = lds_frag(b, wn * WN + j * 16 + frow, fc);
-    float s[TM];
-#pragma unroll
-    for (int i = 0; i < TM; i++) s[i] = sc[wm * WM + i * 16 + frow] * sbv;
+    for (int i = 0; i < TM; i++) r.sa[i] = sc[wm * WM + i * 16 + frow];
+}
 
-    // MFMA k's result is folded three MFMAs later, when it is certainly
-    // ready, so no wait states are needed and only 4 temporaries are live;
-    // the hard scheduling barriers keep the compiler from hoisting MFMAs.
-    constexpr int D = 3;
-    v4f p[D + 1];
-    v8i an = lds_frag(a, wm * WM + frow, fc);
+__device__ __forceinline__ void combine_scales(float (&s)[TM], const RawScales &r) {
+#pragma unroll
+    for (int i = 0; i < TM; i++) s[i] = r.sa[i] * r.sb;
+}
+
+// The first fragments of the K block in stage ST, in the order the first
+// MFMAs use them (A row group 0, then B column groups 0..3), then the scales.
+template <int ST>
+__device__ __forceinline__ void read_head(v8i &a, v8i (&bf)[TN], float (&s)[TM], int wm, int wn,
+                                          int frow, int fc) {
+    a = lds_frag(stA<ST>(), wm * WM + frow, fc);
+#pragma unroll
+    for (int j = 0; j < TN; j++) bf[j] = lds_frag(stB<ST>(), wn * WN + j * 16 + frow, fc);
+    RawScales r;
+    read_scales<ST>(r, wm, wn, frow);
+    combine_scales(s, r);
+}
+
+// One K block from stage ST: 8 x 4 MFMAs per wave, each into a zeroed
+// temporary p[k % 4] that is folded into its accumulator (one fma per
+// element, by the row's combined scale) three MFMAs later, when it is
+// certainly complete.  The fold pipeline runs on across K blocks: the last
+// three products of a block are folded during the first MFMAs of the next,
+// with that block's row-group-7 scale s_tail.
+//
+// The next K block kb + 1 waits in the other stage: after row group 6
+// (every fragment of this stage is then in registers) the waves meet at a
+// barrier, the DMA of block kb + 2 is started into this stage, and the reads
+// of block kb + 1's first fragments and scales go out between the MFMAs of
+// row group 7, so that its MFMAs find them landed.  After the last block
+// those reads fetch unused values and the DMA goes nowhere.
+template <int ST>
+__device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
+                                       v8i (&bf)[TN], float (&s)[TM], const Loader &L, int kb,
+                                       int KB, int wm, int wn, int frow, int fc) {
+    const uint8_t *as = stA<ST>();
+    v8i an = a;
+    v8i a_next = a;
+    RawScales rn;
 #pragma unroll
     for (int i = 0; i < TM; i++) {
         const v8i af = an;
-        if (i + 1 < TM) an = lds_frag(a, wm * WM + (i + 1) * 16 + frow, fc);
+        if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
+        if (i == TM - 1) {
+            wait_dma_and_sync();
+            load_stage<ST>(L, kb + 2, kb + 2 < KB);
+            a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
+            read_scales<ST ^ 1>(rn, wm, wn, frow);
+        }
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int k = i * TN + j;
-            p[k % (D + 1)] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            p[k & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bf[j], af, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-            if (k >= D) {
-                const int kp = k - D;
-                fold4(acc[kp / TN][kp % TN], p[kp % (D + 1)], s[kp / TN]);
+            if (k >= 3) {
+                const int kp = k - 3;
+                fold4(acc[kp / TN][kp % TN], p[kp & 3], s[kp / TN]);
+            } else {
+                // products 29, 30, 31 of the previous block: row group 7
+                fold4(acc[TM - 1][k + 1], p[(k + 1) & 3], s_tail);
             }
+            if (i == TM - 1) bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#pragma unroll
-    for (int kp = TM * TN - D; kp < TM * TN; kp++) fold4(acc[kp / TN][kp % TN], p[kp % (D + 1)], s[kp / TN]);
+    s_tail = s[TM - 1];
+    combine_scales(s, rn);
+    a = a_next;
 }
 
-__device__ __forceinline__ void wait_dma_and_sync() {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
-    __syncthreads();
+static_assert(64 * BN * 2 == BM * BK, "each operand array holds 64 rows of the bf16 output tile");
+
+// Row ml (0..255) of the bf16 output tile staged in LDS: 64 rows in each of
+// the four operand arrays, 512 bytes per row.
+__device__ __forceinline__ uint8_t *out_row(int ml) {
+    const int q = ml >> 6;
+    uint8_t *base = q == 0 ? sA0 : q == 1 ? sA1 : q == 2 ? sB0 : sB1;
+    return base + (ml & 63) * (BN * 2);
 }
 
 __global__ void __launch_bounds__(NTHREADS)
@@ -202,6 +262,7 @@ bsgemm_tile_kernel(GemmArgs g) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
     const int64_t K = g.K;
+    const int KB = g.KB;
 
     // ---- operand descriptors: this tile's row panels, zero past the end ----
     Loader L;
@@ -210,6 +271,7 @@ bsgemm_tile_kernel(GemmArgs g) {
     const int nb0 = (int)(n0 / 128);
     L.rS = wave < 4 ? make_rsrc(g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
                     : make_rsrc(g.sb + (int64_t)nb0 * g.KB, (int64_t)(g.NB - nb0) * g.KB * 4);
+    L.rZ = make_rsrc(g.A, 0);
     L.ldsq = wave * 4096;
     {
         const int row = wave * 32 + (lane >> 3);   // + 8 per slot i
@@ -220,55 +282,81 @@ bsgemm_tile_kernel(GemmArgs g) {
         L.sdst = wave * 256;
     }
 
+    const int frow = lane & 15;
+    const int fc = (lane >> 4) * 2;
+
+    // K block kb sits in stage (kb + KB + 1) % 2, so that the blocks after
+    // an odd first one come in (stage 1, stage 0) pairs.  The first block is
+    // loaded and read before the loop; each block then starts the DMA of the
+    // block after next (see kblock).
+    v8i a, bf[TN];
+    float s[TM];
+    if (KB & 1) {
+        load_stage<0>(L, 0);
+        wait_dma_and_sync();
+        load_stage<1>(L, 1, KB > 1);
+        read_head<0>(a, bf, s, wm, wn, frow, fc);
+    } else {
+        load_stage<1>(L, 0);
+        wait_dma_and_sync();
+        load_stage<0>(L, 1);
+        read_head<1>(a, bf, s, wm, wn, frow, fc);
+    }
 
     v4f acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; i++)
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    // nothing pending before the first block: its first three folds add 0 * 0
+    v4f p[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+    float s_tail = 0.f;
 
-    const int frow = lane & 15;
-    const int fc = (lane >> 4) * 2;
-
-    load_stage<0>(L, 0);
-    wait_dma_and_sync();
-    // K blocks in pairs: stage 0 holds even blocks, stage 1 odd ones; the
-    // next block is DMA'd into the idle stage while the other is consumed.
-    // The last one or two blocks are peeled so the loop body is straight-line.
     int kb = 0;
-    for (; kb + 2 < g.KB; kb += 2) {
-        load_stage<1>(L, kb + 1);
-        compute_stage<0>(acc, wm, wn, frow, fc);
-        wait_dma_and_sync();
-        load_stage<0>(L, kb + 2);
-        compute_stage<1>(acc, wm, wn, frow, fc);
-        wait_dma_and_sync();
+    if (KB & 1) {
+        kblock<0>(acc, p, s_tail, a, bf, s, L, 0, KB, wm, wn, frow, fc);
+        kb = 1;
     }
-    if (kb + 1 < g.KB) {
-        load_stage<1>(L, kb + 1);
-        compute_stage<0>(acc, wm, wn, frow, fc);
-        wait_dma_and_sync();
-        compute_stage<1>(acc, wm, wn, frow, fc);
-    } else {
-        compute_stage<0>(acc, wm, wn, frow, fc);
+    for (; kb < KB; kb += 2) {
+        kblock<1>(acc, p, s_tail, a, bf, s, L, kb, KB, wm, wn, frow, fc);
+        kblock<0>(acc, p, s_tail, a, bf, s, L, kb + 1, KB, wm, wn, frow, fc);
     }
+#pragma unroll
+    for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last (empty) DMA is retired
 
-    // ---- epilogue: lane holds C[m][n .. n+3], m = row of the A sub-tile ----
+    // ---- epilogue ----
+    // The bf16 tile is staged in LDS (the four operand arrays, 64 rows each,
+    // 512 B per row, 32-byte units XOR-swizzled by row) so that the global
+    // stores write whole 512-byte row segments: each store instruction
+    // covers two rows, lane l the 16 bytes at column 8 * (l % 32).
+    __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int64_t m = m0 + wm * WM + i * 16 + frow;
-        if (m >= g.M) continue;
-        const int64_t d = m / g.band_rows;
-        uint16_t *crow = g.C + d * g.band_stride + (m - d * g.band_rows) * g.N;
+        const int ml = wm * WM + i * 16 + frow;
+        uint8_t *row = out_row(ml);
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int64_t n = n0 + wn * WN + j * 16 + (lane >> 4) * 4;
-            if (n >= g.N) continue;
+            const int byte = (wn * WN + j * 16 + (lane >> 4) * 4) * 2;
             uint2 w;
             w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            *(uint2 *)(crow + n) = w;
+            *(uint2 *)(row + (byte ^ ((ml & 15) << 5))) = w;
         }
+    }
+    __syncthreads();
+    const int64_t n = n0 + (lane & 31) * 8;
+#pragma unroll
+    for (int r = 0; r < BM / 8 / 2; r++) {
+        const int ml = wave * (BM / 8) + r * 2 + (lane >> 5);
+        const u32x4 v = *(const u32x4 *)(out_row(ml) + (((lane & 31) * 16) ^ ((ml & 15) << 5)));
+        const int64_t m = m0 + ml;
+        if (m >= g.M || n >= g.N) continue;
+        const int64_t d = m / g.band_rows;
+        uint16_t *crow = g.C + d * g.band_stride + (m - d * g.band_rows) * g.N;
+        *(u32x4 *)(crow + n) = v;
     }
 }
 
