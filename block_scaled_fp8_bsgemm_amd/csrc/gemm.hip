@@ -105,27 +105,43 @@ struct Loader {
 // One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
 // lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
 // logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
-// A block past the end (valid == false) goes through the zero-size
-// descriptor: the loads touch no memory and the stage is not read again.
+// One DMA instruction of a stage load: pieces 0..7 are the A and B slots
+// i = piece / 2 (A for even pieces, B for odd), piece 8 the scales.  A block
+// past the end (valid == false) goes through the zero-size descriptor: the
+// loads touch no memory and the stage is not read again.
+template <int ST, int PIECE>
+__device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
+    const int koff = kb * BK;
+    if (PIECE < 8) {
+        const int i = PIECE >> 1;
+        const int q = L.ldsq + i * 1024;
+        if (PIECE & 1)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rB : L.rZ, (lds_void *)(stB<ST>() + q),
+                                                     16, L.voff + i * L.k8, koff, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rA : L.rZ, (lds_void *)(stA<ST>() + q),
+                                                     16, L.voff + i * L.k8, koff, 0, 0);
+    } else {
+        // waves 0..3: a_scale of rows 64w..64w+63; waves 4..7: b_scale of
+        // the column blocks from the tile's first one on (each wave its own
+        // slot).  No branch: every wave issues exactly one.
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rS : L.rZ,
+                                                 (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
+                                                 L.soff, kb * 4, 0, 0);
+    }
+}
+
+// DMA the K block kb of the A and B panels and of the scales into stage ST.
+// One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
+// lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
+// logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
 template <int ST>
 __device__ __forceinline__ void load_stage(const Loader &L, int kb, bool valid = true) {
-    const int koff = kb * BK;
-    const __amdgpu_buffer_rsrc_t rA = valid ? L.rA : L.rZ;
-    const __amdgpu_buffer_rsrc_t rB = valid ? L.rB : L.rZ;
-    const __amdgpu_buffer_rsrc_t rS = valid ? L.rS : L.rZ;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int q = L.ldsq + i * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void *)(stA<ST>() + q), 16,
-                                                 L.voff + i * L.k8, koff, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void *)(stB<ST>() + q), 16,
-                                                 L.voff + i * L.k8, koff, 0, 0);
-    }
-    // waves 0..3: a_scale of rows 64w..64w+63; waves 4..7: b_scale of the
-    // column blocks from the tile's first one on (each wave its own slot).
-    // No branch: every wave issues exactly one.
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
-                                             L.soff, kb * 4, 0, 0);
+    dma_piece<ST, 0>(L, kb, valid); dma_piece<ST, 1>(L, kb, valid);
+    dma_piece<ST, 2>(L, kb, valid); dma_piece<ST, 3>(L, kb, valid);
+    dma_piece<ST, 4>(L, kb, valid); dma_piece<ST, 5>(L, kb, valid);
+    dma_piece<ST, 6>(L, kb, valid); dma_piece<ST, 7>(L, kb, valid);
+    dma_piece<ST, 8>(L, kb, valid);
 }
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t *st, int r, int fc) {
@@ -189,9 +205,9 @@ __device__ __forceinline__ void read_head(v8i &a, v8i (&bf)[TN], float (&s)[TM],
 //
 // The next K block kb + 1 waits in the other stage: after row group 6
 // (every fragment of this stage is then in registers) the waves meet at a
-// barrier, the DMA of block kb + 2 is started into this stage, and the reads
-// of block kb + 1's first fragments and scales go out between the MFMAs of
-// row group 7, so that its MFMAs find them landed.  After the last block
+// barrier, the DMA of block kb + 2 is started into this stage (spread over
+// the MFMAs of row group 7), and the reads of block kb + 1's first fragments
+// and scales go out between those MFMAs, so that its MFMAs find them landed.  After the last block
 // those reads fetch unused values and the DMA goes nowhere.
 template <int ST>
 __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
@@ -207,7 +223,7 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
         if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
         if (i == TM - 1) {
             wait_dma_and_sync();
-            load_stage<ST>(L, kb + 2, kb + 2 < KB);
+            dma_piece<ST, 8>(L, kb + 2, kb + 2 < KB);
             a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
             read_scales<ST ^ 1>(rn, wm, wn, frow);
         }
@@ -223,7 +239,15 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
                 // products 29, 30, 31 of the previous block: row group 7
                 fold4(acc[TM - 1][k + 1], p[(k + 1) & 3], s_tail);
             }
-            if (i == TM - 1) bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
+            if (i == TM - 1) {
+                bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
+                // the operand DMA of block kb + 2, two instructions per MFMA
+                // so that no wave stalls on a burst of them
+                if (j == 0) { dma_piece<ST, 0>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 1>(L, kb + 2, kb + 2 < KB); }
+                if (j == 1) { dma_piece<ST, 2>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 3>(L, kb + 2, kb + 2 < KB); }
+                if (j == 2) { dma_piece<ST, 4>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 5>(L, kb + 2, kb + 2 < KB); }
+                if (j == 3) { dma_piece<ST, 6>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 7>(L, kb + 2, kb + 2 < KB); }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
