@@ -97,47 +97,42 @@ __device__ __forceinline__ float pack_absmax(u32x4 w) {
     return m;
 }
 
-// One 256-lane workgroup per row; each lane keeps up to CPT packs of the row
-// in registers across the amax reduction (row length N <= 2048 * CPT).
-template <int CPT>
+// One wavefront per row (four rows per workgroup): each lane loads its CPL
+// packs of the row at once (non-temporal: the band is read once), the row
+// amax is a shuffle reduction inside the wavefront (no LDS, no barrier), and
+// the codes are written from registers.  Row length N <= 512 * CPL.
+template <int CPL>
 __global__ void __launch_bounds__(256)
 rowq_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scale,
             int64_t rows, int nch) {
-    __shared__ float red[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const u32x4 *xr = x + row * nch;
-        u32x4 v[CPT];
-        float amax = 0.0f;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const u32x4 *xr = x + row * nch;
+    u32x4 v[CPL];
+    float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int c = tid + 256 * i;
-            if (c < nch) {
-                v[i] = xr[c];
-                amax = fmaxf(amax, pack_absmax(v[i]));
-            }
-        }
-        amax = wave_max(amax);
-        if (lane == 0) red[wave] = amax;
-        __syncthreads();
-        amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();  // red[] is rewritten by the next row
-        const float s = amax / 448.0f;
-        if (tid == 0) scale[row] = s;
-        u32x2 *qr = q + row * nch;
-        if (s == 0.0f) {
+    for (int i = 0; i < CPL; i++) {
+        const int c = lane + 64 * i;
+        if (c < nch) v[i] = __builtin_nontemporal_load(xr + c);
+    }
 #pragma unroll
-            for (int i = 0; i < CPT; i++) {
-                const int c = tid + 256 * i;
-                if (c < nch) qr[c] = (u32x2){0u, 0u};
-            }
-            continue;
-        }
-        const double R = 1.0 / (double)s;
+    for (int i = 0; i < CPL; i++) {
+        const int c = lane + 64 * i;
+        if (c < nch) amax = fmaxf(amax, pack_absmax(v[i]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / 448.0f;
+    if (lane == 0) scale[row] = s;
+    u32x2 *qr = q + row * nch;
+    // an all-zero row has scale 0 and all-zero codes
+    const double R = s != 0.0f ? 1.0 / (double)s : 0.0;
 #pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int c = tid + 256 * i;
-            if (c < nch) qr[c] = quant_pack(v[i], R);
+    for (int i = 0; i < CPL; i++) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            const u32x2 o = s != 0.0f ? quant_pack(v[i], R) : (u32x2){0u, 0u};
+            __builtin_nontemporal_store(o, qr + c);
         }
     }
 }
@@ -186,37 +181,26 @@ __device__ __forceinline__ u32x4 dequant_pack(u32x2 c, float s) {
     return o;
 }
 
-// one 128-lane workgroup per row, UPT packs of 8 codes per lane, all loads
-// issued before the first store
-template <int UPT>
-__global__ void __launch_bounds__(128)
+// A flat grid over the packs of 8 codes (row = pack / nch), two packs per
+// lane with both loads issued before the stores; non-temporal loads and
+// stores (every byte is touched once).  IDX is the pack index type.
+template <typename IDX>
+__global__ void __launch_bounds__(256)
 rowdq_kernel(const u32x2 *__restrict__ q, const float *__restrict__ scale, u32x4 *__restrict__ y,
-             int64_t rows, int nch) {
-    const int tid = threadIdx.x;
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const float s = scale[row];
-        const u32x2 *qr = q + row * nch;
-        u32x4 *yr = y + row * nch;
-        u32x2 v[UPT];
-#pragma unroll
-        for (int i = 0; i < UPT; i++) {
-            const int c = tid + 128 * i;
-            if (c < nch) v[i] = __builtin_nontemporal_load(qr + c);
+             IDX npack, IDX nch) {
+    const IDX stride = (IDX)gridDim.x * 256;
+    for (IDX v0 = (IDX)blockIdx.x * 256 + threadIdx.x; v0 < npack; v0 += 2 * stride) {
+        const IDX v1 = v0 + stride;
+        const u32x2 c0 = __builtin_nontemporal_load(q + v0);
+        const float s0 = scale[v0 / nch];
+        u32x2 c1 = {0u, 0u};
+        float s1 = 0.0f;
+        if (v1 < npack) {
+            c1 = __builtin_nontemporal_load(q + v1);
+            s1 = scale[v1 / nch];
         }
-#pragma unroll
-        for (int i = 0; i < UPT; i++) {
-            const int c = tid + 128 * i;
-            if (c < nch) yr[c] = dequant_pack(v[i], s);
-        }
-    }
-}
-
-__global__ void __launch_bounds__(128)
-rowdq_long_kernel(const u32x2 *__restrict__ q, const float *__restrict__ scale,
-                  u32x4 *__restrict__ y, int64_t rows, int nch) {
-    for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-        const float s = scale[row];
-        for (int c = threadIdx.x; c < nch; c += 128) y[row * nch + c] = dequant_pack(q[row * nch + c], s);
+        __builtin_nontemporal_store(dequant_pack(c0, s0), y + v0);
+        if (v1 < npack) __builtin_nontemporal_store(dequant_pack(c1, s1), y + v1);
     }
 }
 
@@ -340,40 +324,42 @@ int bs_launch_rowq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, in
                    hipStream_t stream) {
     int rc = 0;
     const int nch = (int)(N / 8);
-    const dim3 grid(grid_rows(rows)), block(256);
     const u32x4 *xv = (const u32x4 *)x;
     u32x2 *qv = (u32x2 *)q;
+    if (nch > 2048) {
+        const dim3 grid(grid_rows(rows)), block(256);
+        return bs_enqueue(rowq_long_kernel, grid, block, stream, xv, qv, scale, rows, nch);
+    }
+    const int64_t wg = (rows + 3) / 4;
+    if (wg > 0x7FFFFFFF) return -1;
+    const dim3 grid((unsigned)wg), block(256);
     if (nch <= 256)
-        rc |= bs_enqueue(rowq_kernel<1>, grid, block, stream, xv, qv, scale, rows, nch);
-    else if (nch <= 512)
-        rc |= bs_enqueue(rowq_kernel<2>, grid, block, stream, xv, qv, scale, rows, nch);
-    else if (nch <= 1024)
         rc |= bs_enqueue(rowq_kernel<4>, grid, block, stream, xv, qv, scale, rows, nch);
-    else if (nch <= 2048)
+    else if (nch <= 512)
         rc |= bs_enqueue(rowq_kernel<8>, grid, block, stream, xv, qv, scale, rows, nch);
+    else if (nch <= 896)
+        rc |= bs_enqueue(rowq_kernel<14>, grid, block, stream, xv, qv, scale, rows, nch);
+    else if (nch <= 1024)
+        rc |= bs_enqueue(rowq_kernel<16>, grid, block, stream, xv, qv, scale, rows, nch);
     else
-        rc |= bs_enqueue(rowq_long_kernel, grid, block, stream, xv, qv, scale, rows, nch);
+        rc |= bs_enqueue(rowq_kernel<32>, grid, block, stream, xv, qv, scale, rows, nch);
     return rc;
 }
 
 int bs_launch_rowdq(const uint8_t *q, const float *scale, uint16_t *y, int64_t rows, int64_t N,
                     hipStream_t stream) {
-    int rc = 0;
-    const int nch = (int)(N / 8);
-    const dim3 grid(grid_rows(rows)), block(128);
+    const int64_t nch = N / 8;
+    const int64_t npack = rows * nch;
+    int64_t blocks = (npack + 511) / 512;
+    if (blocks > 1048576) blocks = 1048576;
+    if (blocks < 1) blocks = 1;
     const u32x2 *qv = (const u32x2 *)q;
     u32x4 *yv = (u32x4 *)y;
-    if (nch <= 128)
-        rc |= bs_enqueue(rowdq_kernel<1>, grid, block, stream, qv, scale, yv, rows, nch);
-    else if (nch <= 256)
-        rc |= bs_enqueue(rowdq_kernel<2>, grid, block, stream, qv, scale, yv, rows, nch);
-    else if (nch <= 512)
-        rc |= bs_enqueue(rowdq_kernel<4>, grid, block, stream, qv, scale, yv, rows, nch);
-    else if (nch <= 1024)
-        rc |= bs_enqueue(rowdq_kernel<8>, grid, block, stream, qv, scale, yv, rows, nch);
-    else
-        rc |= bs_enqueue(rowdq_long_kernel, grid, block, stream, qv, scale, yv, rows, nch);
-    return rc;
+    if (npack < 0x7FFFFFFF - 2 * 256 * blocks)
+        return bs_enqueue(rowdq_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), stream, qv, scale,
+                          yv, (uint32_t)npack, (uint32_t)nch);
+    return bs_enqueue(rowdq_kernel<uint64_t>, dim3((unsigned)blocks), dim3(256), stream, qv, scale, yv,
+                      (uint64_t)npack, (uint64_t)nch);
 }
 
 int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
