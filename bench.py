@@ -129,8 +129,9 @@ def streaming_rates(M, N, P, dev, iters=20):
     t = timed(lambda i: bs.band_reduce(red_in[i], red_out[i]), nset)
     b = (P + 1) * band_rows * N * 2
     out["band_reduce"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
-    # rowq: [2048,7168] bf16 -> u8 + scales: 44 MB per call; 24 sets
-    nset = 24
+    # rowq: [2048,7168] bf16 -> u8 + scales: 44 MB per call; 8 sets (352 MB: more
+    # than the Infinity Cache, few enough pages to keep the TLB warm)
+    nset = 8
     rq_in = [red_out[i % len(red_out)] if i < len(red_out) else torch.randn(band_rows, N, device=dev).to(torch.bfloat16)
              for i in range(nset)]
     rq_q = [torch.empty(band_rows, N, dtype=torch.uint8, device=dev) for _ in range(nset)]
