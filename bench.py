@@ -103,7 +103,8 @@ def time_steps(step, steps, warmup):
 
 
 def streaming_rates(M, N, P, dev, iters=20):
-    """band_reduce / rowq / rowdq alone, rotating over buffer sets of > 1 GiB."""
+    """band_reduce / rowq / rowdq / actq alone, rotating over buffer sets larger
+    than the Infinity Cache."""
     import torch
     import block_scaled_fp8_bsgemm_amd as bs
     band_rows = M // P
@@ -150,6 +151,16 @@ def streaming_rates(M, N, P, dev, iters=20):
     b = M * N * 3 + M * 4
     out["rowdq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
     del dq_q, dq_s, dq_y
+    # actq: the bf16 activation [M,K] -> e4m3 + [M,K/128] scales (the GEMM's A);
+    # 102 MB per call; 4 sets
+    nset, K = 4, 2048
+    aq_x = [torch.randn(M, K, device=dev).to(torch.bfloat16) for _ in range(nset)]
+    aq_q = [torch.empty(M, K, dtype=torch.uint8, device=dev) for _ in range(nset)]
+    aq_s = [torch.empty(M, K // 128, dtype=torch.float32, device=dev) for _ in range(nset)]
+    t = timed(lambda i: bs.actq_e4m3(aq_x[i], aq_q[i], aq_s[i]), nset)
+    b = M * K * 3 + M * (K // 128) * 4
+    out["actq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    del aq_x, aq_q, aq_s
     torch.cuda.empty_cache()
     return out
 

@@ -11,6 +11,7 @@ library has not been built, importing the functions raises immediately.
   rowq_e4m3(x, q=None, scale=None)
   rowdq_e4m3(q, scale, y=None)
   blockq_e4m3(x, block_rows, q=None, scale=None)
+  actq_e4m3(x, q=None, scale=None)
 
 Tensors: e4m3 codes are uint8 (or torch.float8_e4m3fn, reinterpreted), bf16
 values are torch.bfloat16 (or int16/uint16 bit patterns), scales float32.
@@ -25,7 +26,8 @@ LIB_PATH = os.path.join(_PKG, "libbsgemm.so")
 BS_OK, BS_ERR_INVALID, BS_ERR_UNSUPPORTED, BS_ERR_LAUNCH = 0, 1, 2, 3
 
 # every extern "C" symbol of include/bsgemm.h
-EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "bs_status_str")
+EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
+           "bs_status_str")
 
 _lib = None
 
@@ -50,7 +52,8 @@ def load():
     L.rowq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
     L.rowdq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
     L.blockq_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
-    for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3"):
+    L.actq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
+    for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3"):
         getattr(L, f).restype = ctypes.c_int
     L.bs_status_str.argtypes = [ctypes.c_int]
     L.bs_status_str.restype = ctypes.c_char_p
@@ -176,4 +179,18 @@ def blockq_e4m3(x, block_rows, q=None, scale=None, stream=None):
     st = load().blockq_e4m3(_ptr(x, _f32(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                             rows, cols, block_rows, _stream(stream))
     _check(st, "blockq_e4m3")
+    return q, scale
+
+
+def actq_e4m3(x, q=None, scale=None, stream=None):
+    """(q uint8 [rows,cols], scale fp32 [rows, cols/128]) = 1x128 e4m3 quantization of bf16 x."""
+    torch = _torch()
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    st = load().actq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
+                          rows, cols, _stream(stream))
+    _check(st, "actq_e4m3")
     return q, scale

@@ -121,4 +121,16 @@ bs_status blockq_e4m3(const float *x, uint8_t *q, float *scale, int64_t rows, in
                                                                                          : BS_ERR_LAUNCH;
 }
 
+bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
+                    void *stream) {
+    if (!x || !q || !scale || rows < 0 || cols <= 0) return BS_ERR_INVALID;
+    if (cols % 128 || cols >= kMaxDim || rows >= kMaxDim) return BS_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return BS_ERR_UNSUPPORTED;
+    const Range rx = range_of(x, rows * cols * 2), rq = range_of(q, rows * cols),
+                rs = range_of(scale, rows * (cols / 128) * 4);
+    if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return BS_ERR_INVALID;
+    if (rows == 0) return BS_OK;
+    return bs_launch_actq(x, q, scale, rows, cols, as_stream(stream)) == 0 ? BS_OK : BS_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -19,6 +19,8 @@ int bs_launch_rowdq(const uint8_t *q, const float *scale, uint16_t *y, int64_t r
 
 int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
                      int block_rows, hipStream_t stream);
+int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
+                   hipStream_t stream);
 
 #include <tuple>
 

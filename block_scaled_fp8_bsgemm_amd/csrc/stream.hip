@@ -12,6 +12,9 @@
 //                dequantize; "Who moves the gather")
 //   blockq_e4m3  fp32 operand -> e4m3 + fp32 scale per 1x128 or 128x128 block
 //                (the blockscale operand format of "Running the benchmark")
+//   actq_e4m3    bf16 activation -> e4m3 + fp32 scale per 1x128 block (sglang
+//                PR 43480, "Numerics, measured where the path engages": a
+//                plain bf16 layer input is quantised by the layer itself)
 //
 // All of them move 16-byte vectors with coalesced, unit-stride accesses and
 // keep each lane's data in registers between the load and the store.
@@ -287,6 +290,34 @@ blockq_128x128_kernel(const float *__restrict__ x, uint8_t *__restrict__ q,
     }
 }
 
+// ------------------------------------------------- activation quantizer --
+
+// bf16 [rows, cols] in 1x128 blocks: each lane takes two adjacent 16-byte
+// packs (16 values), 8 lanes per block, so a block's amax is an 8-lane
+// shuffle reduction and each lane writes 16 bytes of codes.  Blocks are
+// contiguous (cols % 128 == 0), so the flat block index is also the index
+// into the [rows, cols/128] scale array.  Non-temporal loads and stores.
+__global__ void __launch_bounds__(256)
+actq_1x128_kernel(const u32x4 *__restrict__ x, u32x4 *__restrict__ q, float *__restrict__ scale,
+                  uint64_t npair) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    // every lane of an 8-lane block group has the same v < npair: npair and
+    // the stride are multiples of 8
+    for (uint64_t v = (uint64_t)blockIdx.x * 256 + threadIdx.x; v < npair; v += stride) {
+        const u32x4 a = __builtin_nontemporal_load(x + 2 * v);
+        const u32x4 b = __builtin_nontemporal_load(x + 2 * v + 1);
+        float amax = fmaxf(pack_absmax(a), pack_absmax(b));
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+        const float s = amax / 448.0f;
+        if ((v & 7) == 0) scale[v >> 3] = s;
+        const double R = s != 0.0f ? 1.0 / (double)s : 0.0;
+        const u32x2 o0 = s != 0.0f ? quant_pack(a, R) : (u32x2){0u, 0u};
+        const u32x2 o1 = s != 0.0f ? quant_pack(b, R) : (u32x2){0u, 0u};
+        __builtin_nontemporal_store((u32x4){o0[0], o0[1], o1[0], o1[1]}, q + v);
+    }
+}
+
 unsigned grid_rows(int64_t rows) { return (unsigned)(rows < 1048576 ? (rows > 0 ? rows : 1) : 1048576); }
 
 }  // namespace
@@ -379,4 +410,14 @@ int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int
                            x, q, scale, rows, cols);
     }
     return rc;
+}
+
+int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
+                   hipStream_t stream) {
+    const uint64_t npair = (uint64_t)rows * (uint64_t)(cols / 16);
+    uint64_t blocks = (npair + 255) / 256;
+    if (blocks > 1048576) blocks = 1048576;
+    if (blocks < 1) blocks = 1;
+    return bs_enqueue(actq_1x128_kernel, dim3((unsigned)blocks), dim3(256), stream, (const u32x4 *)x,
+                      (u32x4 *)q, scale, npair);
 }

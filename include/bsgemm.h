@@ -9,6 +9,8 @@
  *   rowdq_e4m3   per-row e4m3 dequantize back to bf16
  *   blockq_e4m3  fp32 operand -> e4m3 codes + fp32 block scales (the
  *                activation/weight quantizer that produces bsgemm_fp8's input)
+ *   actq_e4m3    bf16 activation -> e4m3 codes + fp32 1x128 scales (the
+ *                on-GPU step before bsgemm_fp8 when the layer input is bf16)
  *
  * Pages defining the operations (cited by title and section):
  *   [PR40757] sglang PR 40757 "[AMD][gfx950] DSV4: fuse wo_b's GEMM with its
@@ -16,6 +18,9 @@
  *             by an all-reduce of [M, hidden]; each destination's row band
  *             written as its own unit), "Numbers" (fused and unfused agree up
  *             to accumulation order).
+ *   [PR43480] sglang PR 43480 (DeepSeek-V4.1-Flash wo_b): "Numerics,
+ *             measured where the path engages" (on the aiter route wo_b is
+ *             handed a plain bf16 activation and quantises it itself).
  *   [MORI]    "MORI GEMM + All-Reduce Benchmark": "Running the benchmark"
  *             (--quant blockscale: A per 1x128, B per 128x128, fp32 scales;
  *             shape [M,7168], K=2048), "Where the time goes" (reduce /
@@ -166,6 +171,26 @@ bs_status rowdq_e4m3(const uint8_t *q, const float *scale, uint16_t *y,
 bs_status blockq_e4m3(const float *x, uint8_t *q, float *scale,
                       int64_t rows, int64_t cols, int32_t block_rows,
                       void *stream);
+
+/*
+ * Activation quantizer: the bf16 layer input of bsgemm_fp8 quantised on the
+ * GPU, as the layer does when it is handed a plain bf16 tensor ([PR43480]
+ * "Numerics, measured where the path engages"), at the activation
+ * granularity of [MORI] "Running the benchmark" (1x128 blocks, fp32 scales).
+ * For each block of 128 consecutive elements of a row: amax = max |x|;
+ * s = amax / 448 (fp32); codes = e4m3 of the fp32 quotient x / s exactly as
+ * rowq_e4m3 (zero scale -> codes 0x00).  Identical to blockq_e4m3 with
+ * block_rows = 1 on the fp32 values of x (every bf16 value is an fp32 value).
+ *
+ *   x      bf16 [rows, cols] (finite)
+ *   q      e4m3 [rows, cols]
+ *   scale  fp32 [rows, cols/128]
+ *
+ * Requirements: rows >= 0; cols > 0, cols % 128 == 0; x, q 16-byte aligned;
+ * scale 4-byte aligned; no output overlaps x or the other output.
+ */
+bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
+                    int64_t rows, int64_t cols, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *bs_status_str(bs_status status);

@@ -103,3 +103,18 @@ def test_rowq_rowdq_blockq_rejections(L):
     assert L.blockq_e4m3(P, P + 0x100000, 0, 4, 256, 1, None) == INV
     assert L.blockq_e4m3(P, P + 512, P + 0x200000, 4, 256, 1, None) == INV
     assert L.blockq_e4m3(P, P + 0x100000, P + 0x200000, 0, 256, 128, None) == OK
+
+
+def test_actq_rejections(L):
+    f = L.actq_e4m3
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_void_p]
+    assert f(0, P + 0x100000, P + 0x200000, 4, 256, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, -1, 256, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, 4, 0, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, 4, 200, None) == UNS             # cols % 128
+    assert f(P + 8, P + 0x100000, P + 0x200000, 4, 256, None) == UNS         # x alignment
+    assert f(P, P + 0x100000, P + 0x200002, 4, 256, None) == UNS             # scale alignment
+    assert f(P, P + 1024, P + 0x200000, 4, 256, None) == INV                 # q overlaps x (2 KiB)
+    assert f(P, P + 0x100000, P + 0x100000 + 512, 4, 256, None) == INV       # scale overlaps q
+    assert f(P, P + 0x100000, P + 0x200000, 0, 256, None) == OK

@@ -1,5 +1,6 @@
-"""GPU parity of band_reduce, rowq_e4m3, rowdq_e4m3 and blockq_e4m3 against
-the oracle (O6, O7, O8, O3).  All of these are bit-exact: the device takes
+"""GPU parity of band_reduce, rowq_e4m3, rowdq_e4m3, blockq_e4m3 and
+actq_e4m3 against the oracle (O6, O7, O8, O3; actq is O3 with 1x128 blocks on
+the fp32 values of bf16 inputs).  All of these are bit-exact: the device takes
 the same fp32 decisions in the same order as the definition."""
 import numpy as np
 import pytest
@@ -150,3 +151,34 @@ def test_blockq_bitexact(rows, cols, br):
     torch.cuda.synchronize()
     assert np.array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), qr)
+
+
+# ------------------------------------------------------ activation quantizer --
+
+@pytest.mark.parametrize("rows,cols", [(256, 256), (300, 640), (1, 128), (4096, 2048), (16384, 2048)])
+def test_actq_bitexact(rows, cols):
+    say(f"actq_e4m3 rows={rows} cols={cols}")
+    a = synth.operand_fp32(rows, 128, cols, seed=11, heavy=True)[0]   # [rows, cols]
+    bits = oracle.bf16_rne_array(a)
+    bits[min(3, rows - 1), :128] = 0                      # a zero block
+    bits[min(5, rows - 1), 128 * (cols // 128 - 1):] = 0x8000   # a block of -0
+    x32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    qr, sr = oracle.quant_blocks(x32, 1, 128)
+    q = poison_u8(torch.empty((rows, cols), dtype=torch.uint8, device=device()))
+    q, s = bs.actq_e4m3(bf16_dev(bits), q)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+def test_actq_matches_blockq():
+    """The same values through the bf16 and the fp32 quantizer give the same codes."""
+    rows, cols = 512, 1024
+    a = synth.operand_fp32(rows, 128, cols, seed=12, heavy=True)[0]
+    bits = oracle.bf16_rne_array(a)
+    x32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    say("actq vs blockq")
+    q1, s1 = bs.actq_e4m3(bf16_dev(bits))
+    q2, s2 = bs.blockq_e4m3(to_dev(x32), 1)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
