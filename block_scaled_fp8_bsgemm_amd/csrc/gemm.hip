@@ -203,12 +203,14 @@ __device__ __forceinline__ void read_head(v8i &a, v8i (&bf)[TN], float (&s)[TM],
 // three products of a block are folded during the first MFMAs of the next,
 // with that block's row-group-7 scale s_tail.
 //
-// The next K block kb + 1 waits in the other stage: after row group 6
-// (every fragment of this stage is then in registers) the waves meet at a
-// barrier, the DMA of block kb + 2 is started into this stage (spread over
-// the MFMAs of row group 7), and the reads of block kb + 1's first fragments
-// and scales go out between those MFMAs, so that its MFMAs find them landed.  After the last block
-// those reads fetch unused values and the DMA goes nowhere.
+// The next K block kb + 1 goes to the other stage, which nobody reads after
+// the previous block's barrier: its DMA is issued one instruction after each
+// of this block's first nine MFMAs.  After row group 6 (every fragment of this
+// stage is then in registers) each wave waits for its DMA and the waves meet
+// at a barrier; the reads of block kb + 1's first fragments and scales then go
+// out between the MFMAs of row group 7, so that its MFMAs find them landed.
+// After the last block the DMA goes nowhere and those reads fetch unused
+// values.
 template <int ST>
 __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
                                        v8i (&bf)[TN], float (&s)[TM], const Loader &L, int kb,
@@ -223,7 +225,6 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
         if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
         if (i == TM - 1) {
             wait_dma_and_sync();
-            dma_piece<ST, 8>(L, kb + 2, kb + 2 < KB);
             a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
             read_scales<ST ^ 1>(rn, wm, wn, frow);
         }
@@ -241,12 +242,21 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             }
             if (i == TM - 1) {
                 bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
-                // the operand DMA of block kb + 2, two instructions per MFMA
-                // so that no wave stalls on a burst of them
-                if (j == 0) { dma_piece<ST, 0>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 1>(L, kb + 2, kb + 2 < KB); }
-                if (j == 1) { dma_piece<ST, 2>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 3>(L, kb + 2, kb + 2 < KB); }
-                if (j == 2) { dma_piece<ST, 4>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 5>(L, kb + 2, kb + 2 < KB); }
-                if (j == 3) { dma_piece<ST, 6>(L, kb + 2, kb + 2 < KB); dma_piece<ST, 7>(L, kb + 2, kb + 2 < KB); }
+            }
+            // the DMA of block kb + 1 into the other stage (unread since the
+            // previous block's barrier), one instruction after each of the
+            // first nine MFMAs, away from the head reads of row group 7
+            if (k < 9) {
+                const bool v = kb + 1 < KB;
+                if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
+                if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
+                if (k == 2) dma_piece<ST ^ 1, 1>(L, kb + 1, v);
+                if (k == 3) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
+                if (k == 4) dma_piece<ST ^ 1, 3>(L, kb + 1, v);
+                if (k == 5) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
+                if (k == 6) dma_piece<ST ^ 1, 5>(L, kb + 1, v);
+                if (k == 7) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
+                if (k == 8) dma_piece<ST ^ 1, 7>(L, kb + 1, v);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -312,18 +322,16 @@ bsgemm_tile_kernel(GemmArgs g) {
     // K block kb sits in stage (kb + KB + 1) % 2, so that the blocks after
     // an odd first one come in (stage 1, stage 0) pairs.  The first block is
     // loaded and read before the loop; each block then starts the DMA of the
-    // block after next (see kblock).
+    // next one (see kblock).
     v8i a, bf[TN];
     float s[TM];
     if (KB & 1) {
         load_stage<0>(L, 0);
         wait_dma_and_sync();
-        load_stage<1>(L, 1, KB > 1);
         read_head<0>(a, bf, s, wm, wn, frow, fc);
     } else {
         load_stage<1>(L, 0);
         wait_dma_and_sync();
-        load_stage<0>(L, 1);
         read_head<1>(a, bf, s, wm, wn, frow, fc);
     }
 
