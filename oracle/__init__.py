@@ -85,6 +85,11 @@ def lib():
         L.orc_rowq.argtypes = [_u16p, _i64, _i64, _u8p, _f32p]
         L.orc_rowdq.restype = ctypes.c_int
         L.orc_rowdq.argtypes = [_u8p, _f32p, _i64, _i64, _u16p]
+        L.orc_mx_quant.restype = ctypes.c_int
+        L.orc_mx_quant.argtypes = [_f32p, _i64, _i64, _u8p, _u8p]
+        L.orc_mxgemm.restype = ctypes.c_int
+        L.orc_mxgemm.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, ctypes.c_int,
+                                 _i64p, _i64p, _i64, _f32p, _u16p]
         L.orc_threads.restype = ctypes.c_int
         L.orc_threads.argtypes = []
         _lib = L
@@ -244,3 +249,42 @@ def bf16_to_f64(b):
     """Widen an array of bf16 bit patterns (uint16) to float64 (exact)."""
     b = np.asarray(b, np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def mx_quant(x):
+    """O10: fp32 [rows, cols] -> (codes uint8 [rows, cols], E8M0 scale bytes uint8 [rows, cols/32])."""
+    x = np.ascontiguousarray(x, np.float32)
+    rows, cols = x.shape
+    q = np.empty((rows, cols), np.uint8)
+    e = np.empty((rows, cols // 32), np.uint8)
+    _check(lib().orc_mx_quant(_p(x, _f32p), rows, cols, _p(q, _u8p), _p(e, _u8p)), "mx_quant")
+    return q, e
+
+
+def mxgemm(qa, ea, qb, eb, mfma=False):
+    """O11 (exact) or O11m (mfma=True): (acc fp32 [M,N], c bf16 bits [M,N])."""
+    qa, qb = np.ascontiguousarray(qa, np.uint8), np.ascontiguousarray(qb, np.uint8)
+    ea, eb = np.ascontiguousarray(ea, np.uint8), np.ascontiguousarray(eb, np.uint8)
+    M, K = qa.shape
+    N = qb.shape[0]
+    acc = np.empty((M, N), np.float32)
+    c = np.empty((M, N), np.uint16)
+    _check(lib().orc_mxgemm(_p(qa, _u8p), _p(ea, _u8p), _p(qb, _u8p), _p(eb, _u8p), M, N, K, int(mfma),
+                            None, None, 0, _p(acc, _f32p), _p(c, _u16p)), "mxgemm")
+    return acc, c
+
+
+def mxgemm_elems(qa, ea, qb, eb, mi, ni, mfma=False):
+    """O11 / O11m at the sampled elements (mi[i], ni[i]): (acc fp32 [count], c bf16 bits [count])."""
+    qa, qb = np.ascontiguousarray(qa, np.uint8), np.ascontiguousarray(qb, np.uint8)
+    ea, eb = np.ascontiguousarray(ea, np.uint8), np.ascontiguousarray(eb, np.uint8)
+    mi = np.ascontiguousarray(mi, np.int64)
+    ni = np.ascontiguousarray(ni, np.int64)
+    M, K = qa.shape
+    N = qb.shape[0]
+    acc = np.empty(mi.size, np.float32)
+    c = np.empty(mi.size, np.uint16)
+    _check(lib().orc_mxgemm(_p(qa, _u8p), _p(ea, _u8p), _p(qb, _u8p), _p(eb, _u8p), M, N, K, int(mfma),
+                            _p(mi, _i64p), _p(ni, _i64p), mi.size, _p(acc, _f32p), _p(c, _u16p)),
+           "mxgemm_elems")
+    return acc, c
