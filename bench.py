@@ -10,7 +10,8 @@ TFLOP/s (2*M*N*K per step / step time); `phases` gives each kernel's own
 average time and rate inside the timed steps; `roofline` is the GEMM's
 (measured with HIP events on the launch stream); `streaming` gives the
 HBM-bound kernels measured alone on rotating buffers (>1 GiB, so the 256 MB
-Infinity Cache cannot serve repeats); `cpu_baseline` is the CPU oracle timed
+Infinity Cache cannot serve repeats); `mxfp8_gemm` is the mxfp8 variant of the
+GEMM alone at M=16384, N=5120, K=2048; `cpu_baseline` is the CPU oracle timed
 on a bounded row sample of the same workload and projected to a full step.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
@@ -160,9 +161,50 @@ def streaming_rates(M, N, P, dev, iters=20):
     t = timed(lambda i: bs.actq_e4m3(aq_x[i], aq_q[i], aq_s[i]), nset)
     b = M * K * 3 + M * (K // 128) * 4
     out["actq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
-    del aq_x, aq_q, aq_s
+    # mxq: the bf16 operand [M,K] -> e4m3 + [M,K/32] E8M0 bytes (mxgemm's A);
+    # 101 MB per call; 4 sets
+    mq_q = aq_q
+    mq_s = [torch.empty(M, K // 32, dtype=torch.uint8, device=dev) for _ in range(nset)]
+    t = timed(lambda i: bs.mxq_e4m3(aq_x[i], mq_q[i], mq_s[i]), nset)
+    b = M * K * 3 + M * (K // 32)
+    out["mxq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    del aq_x, aq_q, aq_s, mq_s
     torch.cuda.empty_cache()
     return out
+
+
+def mx_gemm_rate(dev, iters=20):
+    """The mxfp8 variant of the GEMM alone at M=16384, N=5120, K=2048 (one
+    band), seeded random codes with E8M0 scales around 2^0."""
+    import torch
+    import block_scaled_fp8_bsgemm_amd as bs
+    M, N, K = 16384, 5120, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    qa = torch.randint(0, 0x7E, (M, K), dtype=torch.uint8, device=dev, generator=g)
+    qa |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    qb = torch.randint(0, 0x7E, (N, K), dtype=torch.uint8, device=dev, generator=g)
+    qb |= torch.randint(0, 2, (N, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    ea = torch.randint(117, 128, (M, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    eb = torch.randint(117, 128, (N, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    s = torch.cuda.current_stream(dev)
+    for _ in range(3):
+        bs.mxgemm_fp8(qa, ea, qb, eb, C, stream=s)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(iters):
+        bs.mxgemm_fp8(qa, ea, qb, eb, C, stream=s)
+    e1.record(s)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / iters * 1e-3
+    tf = 2.0 * M * N * K / t / 1e12
+    del qa, qb, ea, eb, C
+    torch.cuda.empty_cache()
+    return {"kernel": "mxgemm_tile_kernel", "M": M, "N": N, "K": K, "us": t * 1e6, "TFLOP/s": tf,
+            "frac_fp8_peak": tf / PEAK_FP8_TFLOPS, "pages_gemm_only_us": 180.2}
 
 
 def cpu_baseline(M, N, K, P, target_s=10.0):
@@ -292,6 +334,8 @@ def main():
         del step, parts, wq, ws
         torch.cuda.empty_cache()
         rec["streaming"] = streaming_rates(M, N, P, dev)
+        print("[bench] mxfp8 GEMM alone", file=sys.stderr, flush=True)
+        rec["mxfp8_gemm"] = mx_gemm_rate(dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu_baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(M, N, K, P)

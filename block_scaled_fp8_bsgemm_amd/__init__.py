@@ -12,6 +12,8 @@ library has not been built, importing the functions raises immediately.
   rowdq_e4m3(q, scale, y=None)
   blockq_e4m3(x, block_rows, q=None, scale=None)
   actq_e4m3(x, q=None, scale=None)
+  mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0)
+  mxq_e4m3(x, q=None, scale=None)
 
 Tensors: e4m3 codes are uint8 (or torch.float8_e4m3fn, reinterpreted), bf16
 values are torch.bfloat16 (or int16/uint16 bit patterns), scales float32.
@@ -27,7 +29,7 @@ BS_OK, BS_ERR_INVALID, BS_ERR_UNSUPPORTED, BS_ERR_LAUNCH = 0, 1, 2, 3
 
 # every extern "C" symbol of include/bsgemm.h
 EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
-           "bs_status_str")
+           "mxgemm_fp8", "mxq_e4m3", "bs_status_str")
 
 _lib = None
 
@@ -53,7 +55,10 @@ def load():
     L.rowdq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
     L.blockq_e4m3.argtypes = [vp, vp, vp, i64, i64, i32, vp]
     L.actq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
-    for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3"):
+    L.mxgemm_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp]
+    L.mxq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
+    for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
+              "mxgemm_fp8", "mxq_e4m3"):
         getattr(L, f).restype = ctypes.c_int
     L.bs_status_str.argtypes = [ctypes.c_int]
     L.bs_status_str.restype = ctypes.c_char_p
@@ -193,4 +198,35 @@ def actq_e4m3(x, q=None, scale=None, stream=None):
     st = load().actq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                           rows, cols, _stream(stream))
     _check(st, "actq_e4m3")
+    return q, scale
+
+
+def mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0, stream=None):
+    """C (bf16) = mx(A [M,K] e4m3, a_scale u8 [M,K/32]) x mx(B [N,K] e4m3, b_scale u8 [N,K/32])^T,
+    E8M0 scales per 1x32 block, written as `bands` destination-major row bands."""
+    torch = _torch()
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        band_rows = M // bands if bands > 0 else 0
+        stride = band_stride if band_stride else band_rows * N
+        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+    st = load().mxgemm_fp8(_ptr(A, _u8(), "A"), _ptr(a_scale, _u8(), "a_scale"),
+                           _ptr(B, _u8(), "B"), _ptr(b_scale, _u8(), "b_scale"),
+                           _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
+    _check(st, "mxgemm_fp8")
+    return C
+
+
+def mxq_e4m3(x, q=None, scale=None, stream=None):
+    """(q uint8 [rows,cols], scale E8M0 uint8 [rows, cols/32]) = 1x32 mxfp8 quantization of bf16 x."""
+    torch = _torch()
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    st = load().mxq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _u8(), "scale"),
+                         rows, cols, _stream(stream))
+    _check(st, "mxq_e4m3")
     return q, scale

@@ -68,6 +68,32 @@ bs_status bsgemm_fp8(const uint8_t *A, const float *a_scale, const uint8_t *B, c
                : BS_ERR_LAUNCH;
 }
 
+bs_status mxgemm_fp8(const uint8_t *A, const uint8_t *a_scale, const uint8_t *B, const uint8_t *b_scale,
+                     uint16_t *C, int64_t M, int64_t N, int64_t K, int32_t bands,
+                     int64_t band_stride, void *stream) {
+    if (!A || !a_scale || !B || !b_scale || !C) return BS_ERR_INVALID;
+    if (M < 0 || N <= 0 || K <= 0 || bands < 1 || band_stride < 0) return BS_ERR_INVALID;
+    if (N % 128 || K % 128 || bands > 64) return BS_ERR_UNSUPPORTED;
+    if (M >= kMaxDim || N >= kMaxDim || K > kMaxK) return BS_ERR_UNSUPPORTED;
+    if (M % bands) return BS_ERR_UNSUPPORTED;
+    const int64_t band_rows = M / bands;
+    const int64_t stride = band_stride == 0 ? band_rows * N : band_stride;
+    if (stride < band_rows * N || stride % 8) return BS_ERR_UNSUPPORTED;
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(a_scale, 4) ||
+        !aligned(b_scale, 4))
+        return BS_ERR_UNSUPPORTED;
+    const int64_t KQ = K / 32;
+    const Range rc = range_of(C, ((bands - 1) * stride + band_rows * N) * 2);
+    if (overlap(rc, range_of(A, M * K)) || overlap(rc, range_of(B, N * K)) ||
+        overlap(rc, range_of(a_scale, M * KQ)) || overlap(rc, range_of(b_scale, N * KQ)))
+        return BS_ERR_INVALID;
+    if (M == 0) return BS_OK;
+    return bs_launch_mxgemm(A, a_scale, B, b_scale, C, M, N, K, band_rows == 0 ? 1 : band_rows,
+                            stride, as_stream(stream)) == 0
+               ? BS_OK
+               : BS_ERR_LAUNCH;
+}
+
 bs_status band_reduce(const uint16_t *const *parts, int32_t P, uint16_t *out, int64_t rows,
                       int64_t N, void *stream) {
     if (!parts || !out || P < 1 || P > 16 || rows < 0 || N <= 0) return BS_ERR_INVALID;
@@ -131,6 +157,18 @@ bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, i
     if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return BS_ERR_INVALID;
     if (rows == 0) return BS_OK;
     return bs_launch_actq(x, q, scale, rows, cols, as_stream(stream)) == 0 ? BS_OK : BS_ERR_LAUNCH;
+}
+
+bs_status mxq_e4m3(const uint16_t *x, uint8_t *q, uint8_t *scale, int64_t rows, int64_t cols,
+                   void *stream) {
+    if (!x || !q || !scale || rows < 0 || cols <= 0) return BS_ERR_INVALID;
+    if (cols % 32 || cols >= kMaxDim || rows >= kMaxDim) return BS_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(q, 16)) return BS_ERR_UNSUPPORTED;
+    const Range rx = range_of(x, rows * cols * 2), rq = range_of(q, rows * cols),
+                rs = range_of(scale, rows * (cols / 32));
+    if (overlap(rq, rx) || overlap(rs, rx) || overlap(rq, rs)) return BS_ERR_INVALID;
+    if (rows == 0) return BS_OK;
+    return bs_launch_mxq(x, q, scale, rows, cols, as_stream(stream)) == 0 ? BS_OK : BS_ERR_LAUNCH;
 }
 
 }  // extern "C"

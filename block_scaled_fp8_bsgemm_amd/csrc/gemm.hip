@@ -30,6 +30,12 @@
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
 //    in groups of 8 M-tiles so that concurrently running tiles share A and B
 //    panels in that XCD's L2.
+//
+// The same tile kernel is also built for the mxfp8 variant (sglang PR 43480,
+// "What" and "Not in this PR": e4m3 operands with one E8M0 scale byte per
+// 1x32 block of A's and B's rows): there the scales are applied by the scaled
+// MFMA v_mfma_scale_f32_16x16x128_f8f6f4 itself, the MFMAs accumulate
+// directly, and the stage's scale piece carries the tile rows' scale bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -52,9 +58,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct GemmArgs {
     const uint8_t *A;
-    const float *sa;
+    const void *sa;         // blockscale: fp32 [M, K/128]; mxfp8: E8M0 bytes [M, K/32]
     const uint8_t *B;
-    const float *sb;
+    const void *sb;         // blockscale: fp32 [N/128, K/128]; mxfp8: E8M0 bytes [N, K/32]
     uint16_t *C;
     int64_t M, N, K;
     int64_t band_rows, band_stride;
@@ -70,9 +76,11 @@ __shared__ __attribute__((aligned(1024))) uint8_t sA0[BM * BK];
 __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * BK];
 __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * BK];
-// scales per stage: [0, 256) a_scale of the tile's rows; [256, 512) four 64-entry
-// slots filled by waves 4..7 with b_scale, of which entries 256 and 257 (the
-// tile's two 128-column blocks) are read
+// scales per stage, one dword per entry: blockscale: [0, 256) a_scale of the
+// tile's rows; [256, 512) four 64-entry slots filled by waves 4..7 with
+// b_scale, of which entries 256 and 257 (the tile's two 128-column blocks) are
+// read.  mxfp8: [0, 256) the K block's 4 E8M0 bytes of each A row, [256, 512)
+// those of each B row.
 constexpr int SCALES = BM + 256;
 __shared__ __attribute__((aligned(1024))) float sS0[SCALES];
 __shared__ __attribute__((aligned(1024))) float sS1[SCALES];
@@ -101,10 +109,6 @@ struct Loader {
     int sdst;    // byte offset of this wave's 256-byte scale slot (waves 0..4)
 };
 
-// DMA the K block kb of the A and B panels and of the A scales into stage ST.
-// One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
-// lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
-// logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
 // One DMA instruction of a stage load: pieces 0..7 are the A and B slots
 // i = piece / 2 (A for even pieces, B for odd), piece 8 the scales.  A block
 // past the end (valid == false) goes through the zero-size descriptor: the
@@ -122,9 +126,11 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rA : L.rZ, (lds_void *)(stA<ST>() + q),
                                                      16, L.voff + i * L.k8, koff, 0, 0);
     } else {
-        // waves 0..3: a_scale of rows 64w..64w+63; waves 4..7: b_scale of
-        // the column blocks from the tile's first one on (each wave its own
-        // slot).  No branch: every wave issues exactly one.
+        // blockscale: waves 0..3 fetch a_scale of rows 64w..64w+63, waves
+        // 4..7 b_scale of the column blocks from the tile's first one on;
+        // mxfp8: waves 0..3 fetch the 4 scale bytes of the K block for A rows
+        // 64w.., waves 4..7 for B rows 64(w-4)..  Each wave fills its own
+        // 256-byte slot; no branch: every wave issues exactly one.
         __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rS : L.rZ,
                                                  (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
                                                  L.soff, kb * 4, 0, 0);
@@ -196,6 +202,96 @@ __device__ __forceinline__ void read_head(v8i &a, v8i (&bf)[TN], float (&s)[TM],
     combine_scales(s, r);
 }
 
+// ---- mxfp8 --------------------------------------------------------------
+// The scaled MFMA takes lane l's 32 bytes of a 16-row fragment as the K
+// values [16g, 16g+16) and [64+16g, 64+16g+16) of row l%16 (g = l/16), and
+// lane l's scale byte as the E8M0 scale of that row's 32-wide block g.  So an
+// mxfp8 fragment is chunks g and g+4 of the row's 128-byte K segment, and the
+// lane's scale is byte g of the row's 4 scale bytes for the K block.
+__device__ __forceinline__ v8i lds_frag_mx(const uint8_t *st, int r, int g) {
+    const u32x4 lo = *(const u32x4 *)(st + swz(r, g));
+    const u32x4 hi = *(const u32x4 *)(st + swz(r, g + 4));
+    return (v8i){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+struct MxScales {
+    int a[TM];   // A rows of the wave's 8 row groups
+    int b[TN];   // B rows of its 4 column groups
+};
+
+template <int ST>
+__device__ __forceinline__ void read_mx_scales(MxScales &x, int wm, int wn, int frow, int g) {
+    const uint8_t *sc = (const uint8_t *)stS<ST>();
+#pragma unroll
+    for (int i = 0; i < TM; i++) x.a[i] = sc[(wm * WM + i * 16 + frow) * 4 + g];
+#pragma unroll
+    for (int j = 0; j < TN; j++) x.b[j] = sc[(BM + wn * WN + j * 16 + frow) * 4 + g];
+}
+
+template <int ST>
+__device__ __forceinline__ void read_head_mx(v8i &a, v8i (&bf)[TN], MxScales &x, int wm, int wn,
+                                             int frow, int g) {
+    a = lds_frag_mx(stA<ST>(), wm * WM + frow, g);
+#pragma unroll
+    for (int j = 0; j < TN; j++) bf[j] = lds_frag_mx(stB<ST>(), wn * WN + j * 16 + frow, g);
+    read_mx_scales<ST>(x, wm, wn, frow, g);
+}
+
+// DMA of block kb + 1 into stage ST ^ 1 during the first nine MFMAs of block
+// kb (see kblock).
+template <int ST>
+__device__ __forceinline__ void dma_next(const Loader &L, int k, int kb, int KB) {
+    if (k < 9) {
+        const bool v = kb + 1 < KB;
+        if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
+        if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
+        if (k == 2) dma_piece<ST ^ 1, 1>(L, kb + 1, v);
+        if (k == 3) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
+        if (k == 4) dma_piece<ST ^ 1, 3>(L, kb + 1, v);
+        if (k == 5) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
+        if (k == 6) dma_piece<ST ^ 1, 5>(L, kb + 1, v);
+        if (k == 7) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
+        if (k == 8) dma_piece<ST ^ 1, 7>(L, kb + 1, v);
+    }
+}
+
+// One mxfp8 K block from stage ST: the same schedule as the blockscale kblock
+// below (A fragments one row group ahead, barrier after row group 6, the next
+// block's head read between the MFMAs of row group 7, its DMA during the
+// first nine MFMAs), but the block scales are applied inside the MFMA and
+// each MFMA accumulates straight into its accumulator: no fold.
+template <int ST>
+__device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[TN], MxScales &x,
+                                          const Loader &L, int kb, int KB, int wm, int wn, int frow,
+                                          int g) {
+    const uint8_t *as = stA<ST>();
+    v8i an = a;
+    v8i a_next = a;
+    MxScales xn;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const v8i af = an;
+        if (i + 1 < TM) an = lds_frag_mx(as, wm * WM + (i + 1) * 16 + frow, g);
+        if (i == TM - 1) {
+            wait_dma_and_sync();
+            a_next = lds_frag_mx(stA<ST ^ 1>(), wm * WM + frow, g);
+            read_mx_scales<ST ^ 1>(xn, wm, wn, frow, g);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int k = i * TN + j;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bf[j], af, acc[i][j], 0, 0, 0, x.b[j], 0, x.a[i]);
+            if (i == TM - 1) bf[j] = lds_frag_mx(stB<ST ^ 1>(), wn * WN + j * 16 + frow, g);
+            dma_next<ST>(L, k, kb, KB);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    x = xn;
+    a = a_next;
+}
+
 // One K block from stage ST: 8 x 4 MFMAs per wave, each into a zeroed
 // temporary p[k % 4] that is folded into its accumulator (one fma per
 // element, by the row's combined scale) three MFMAs later, when it is
@@ -246,18 +342,7 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             // the DMA of block kb + 1 into the other stage (unread since the
             // previous block's barrier), one instruction after each of the
             // first nine MFMAs, away from the head reads of row group 7
-            if (k < 9) {
-                const bool v = kb + 1 < KB;
-                if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
-                if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
-                if (k == 2) dma_piece<ST ^ 1, 1>(L, kb + 1, v);
-                if (k == 3) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
-                if (k == 4) dma_piece<ST ^ 1, 3>(L, kb + 1, v);
-                if (k == 5) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
-                if (k == 6) dma_piece<ST ^ 1, 5>(L, kb + 1, v);
-                if (k == 7) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
-                if (k == 8) dma_piece<ST ^ 1, 7>(L, kb + 1, v);
-            }
+            dma_next<ST>(L, k, kb, KB);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -276,8 +361,10 @@ __device__ __forceinline__ uint8_t *out_row(int ml) {
     return base + (ml & 63) * (BN * 2);
 }
 
-__global__ void __launch_bounds__(NTHREADS)
-bsgemm_tile_kernel(GemmArgs g) {
+// One 256x256 output tile; MX selects the mxfp8 operands (E8M0 scales per
+// 1x32 block, applied by the scaled MFMA) instead of the blockscale ones.
+template <bool MX>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     // ---- workgroup -> tile (XCD-aware, grouped) ----
     const int T = g.tiles_m * g.tiles_n;
     const int per_xcd = (T + NUM_XCD - 1) / NUM_XCD;
@@ -302,9 +389,16 @@ bsgemm_tile_kernel(GemmArgs g) {
     Loader L;
     L.rA = make_rsrc(g.A + m0 * K, (g.M - m0) * K);
     L.rB = make_rsrc(g.B + n0 * K, (g.N - n0) * K);
-    const int nb0 = (int)(n0 / 128);
-    L.rS = wave < 4 ? make_rsrc(g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
-                    : make_rsrc(g.sb + (int64_t)nb0 * g.KB, (int64_t)(g.NB - nb0) * g.KB * 4);
+    const int KQ = (int)(K / 32);   // mxfp8 scale bytes per row
+    if (MX) {
+        L.rS = wave < 4 ? make_rsrc((const uint8_t *)g.sa + m0 * KQ, (g.M - m0) * KQ)
+                        : make_rsrc((const uint8_t *)g.sb + n0 * KQ, (g.N - n0) * KQ);
+    } else {
+        const int nb0 = (int)(n0 / 128);
+        L.rS = wave < 4 ? make_rsrc((const float *)g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
+                        : make_rsrc((const float *)g.sb + (int64_t)nb0 * g.KB,
+                                    (int64_t)(g.NB - nb0) * g.KB * 4);
+    }
     L.rZ = make_rsrc(g.A, 0);
     L.ldsq = wave * 4096;
     {
@@ -312,12 +406,41 @@ bsgemm_tile_kernel(GemmArgs g) {
         const int chunk = (lane & 7) ^ (lane >> 3);
         L.voff = row * (int)K + chunk * 16;
         L.k8 = 8 * (int)K;
-        L.soff = ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
+        L.soff = MX ? ((wave & 3) * 64 + lane) * KQ : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
         L.sdst = wave * 256;
     }
 
     const int frow = lane & 15;
     const int fc = (lane >> 4) * 2;
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    if constexpr (MX) {
+        const int gq = lane >> 4;
+        v8i a, bf[TN];
+        MxScales x;
+        if (KB & 1) {
+            load_stage<0>(L, 0);
+            wait_dma_and_sync();
+            read_head_mx<0>(a, bf, x, wm, wn, frow, gq);
+        } else {
+            load_stage<1>(L, 0);
+            wait_dma_and_sync();
+            read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
+        }
+        int kb = 0;
+        if (KB & 1) {
+            kblock_mx<0>(acc, a, bf, x, L, 0, KB, wm, wn, frow, gq);
+            kb = 1;
+        }
+        for (; kb < KB; kb += 2) {
+            kblock_mx<1>(acc, a, bf, x, L, kb, KB, wm, wn, frow, gq);
+            kblock_mx<0>(acc, a, bf, x, L, kb + 1, KB, wm, wn, frow, gq);
+        }
+    } else {
 
     // K block kb sits in stage (kb + KB + 1) % 2, so that the blocks after
     // an odd first one come in (stage 1, stage 0) pairs.  The first block is
@@ -335,11 +458,6 @@ bsgemm_tile_kernel(GemmArgs g) {
         read_head<1>(a, bf, s, wm, wn, frow, fc);
     }
 
-    v4f acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; i++)
-#pragma unroll
-        for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     // nothing pending before the first block: its first three folds add 0 * 0
     v4f p[4];
 #pragma unroll
@@ -357,6 +475,7 @@ bsgemm_tile_kernel(GemmArgs g) {
     }
 #pragma unroll
     for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last (empty) DMA is retired
 
     // ---- epilogue ----
@@ -392,11 +511,15 @@ bsgemm_tile_kernel(GemmArgs g) {
     }
 }
 
+__global__ void __launch_bounds__(NTHREADS) bsgemm_tile_kernel(GemmArgs g) { gemm_tile<false>(g); }
+
+__global__ void __launch_bounds__(NTHREADS) mxgemm_tile_kernel(GemmArgs g) { gemm_tile<true>(g); }
+
 }  // namespace
 
-int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb,
-                   uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
-                   int64_t band_stride, hipStream_t stream) {
+static GemmArgs gemm_args(const uint8_t *A, const void *sa, const uint8_t *B, const void *sb,
+                          uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                          int64_t band_stride) {
     GemmArgs g;
     g.A = A; g.sa = sa; g.B = B; g.sb = sb; g.C = C;
     g.M = M; g.N = N; g.K = K;
@@ -405,7 +528,24 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
     g.NB = (int)(N / 128);
     g.tiles_m = (int)((M + BM - 1) / BM);
     g.tiles_n = (int)((N + BN - 1) / BN);
+    return g;
+}
+
+static int gemm_grid(const GemmArgs &g) {
     const int T = g.tiles_m * g.tiles_n;
-    const int grid = ((T + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
-    return bs_enqueue(bsgemm_tile_kernel, dim3(grid), dim3(NTHREADS), stream, g);
+    return ((T + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
+}
+
+int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb,
+                   uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                   int64_t band_stride, hipStream_t stream) {
+    const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
+    return bs_enqueue(bsgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
+}
+
+int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, const uint8_t *sb,
+                     uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                     int64_t band_stride, hipStream_t stream) {
+    const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
+    return bs_enqueue(mxgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
 }

@@ -8,6 +8,9 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
                    uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                    int64_t band_stride, hipStream_t stream);
 
+int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, const uint8_t *sb,
+                     uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                     int64_t band_stride, hipStream_t stream);
 int bs_launch_band_reduce(const uint16_t *const *parts, int P, uint16_t *out, int64_t rows,
                           int64_t N, hipStream_t stream);
 
@@ -21,6 +24,8 @@ int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int
                      int block_rows, hipStream_t stream);
 int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
                    hipStream_t stream);
+int bs_launch_mxq(const uint16_t *x, uint8_t *q, uint8_t *e, int64_t rows, int64_t cols,
+                  hipStream_t stream);
 
 #include <tuple>
 

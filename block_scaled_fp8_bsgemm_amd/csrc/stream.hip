@@ -12,6 +12,8 @@
 //                dequantize; "Who moves the gather")
 //   blockq_e4m3  fp32 operand -> e4m3 + fp32 scale per 1x128 or 128x128 block
 //                (the blockscale operand format of "Running the benchmark")
+//   mxq_e4m3     bf16 -> e4m3 + E8M0 scale per 1x32 block (the mxfp8 operand
+//                format of sglang PR 43480, "Not in this PR")
 //   actq_e4m3    bf16 activation -> e4m3 + fp32 scale per 1x128 block (sglang
 //                PR 43480, "Numerics, measured where the path engages": a
 //                plain bf16 layer input is quantised by the layer itself)
@@ -318,6 +320,53 @@ actq_1x128_kernel(const u32x4 *__restrict__ x, u32x4 *__restrict__ q, float *__r
     }
 }
 
+// ------------------------------------------------------ mxfp8 quantizer --
+
+// bf16 [rows, cols] in 1x32 blocks: one 16-byte pack (8 values) per lane, 4
+// lanes per block (amax by two shuffles).  The block scale is 2^k with k the
+// smallest integer such that amax <= 448 * 2^k, read off amax's IEEE bits:
+// amax = 1.f * 2^E fits under 1.75 * 2^(E+1) = 448 * 2^(E-7) exactly when
+// 1.f <= 1.75, i.e. when the fraction bits are <= 0x600000, else k = E - 7.
+// The codes are e4m3 RNE of x * 2^-k (an exact scaling; results below the
+// fp32 normal range encode to zero either way).  A zero block gets scale
+// byte 0 and codes 0x00.  Two packs per lane, non-temporal loads and stores.
+__device__ __forceinline__ void mxq_pack(u32x4 w, u32x2 *q, uint8_t *e, uint64_t v, bool live) {
+    float amax = live ? pack_absmax(w) : 0.0f;
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    if (!live) return;
+    const uint32_t bits = __float_as_uint(amax);
+    const int ef = (int)(bits >> 23);
+    int k = ef == 0 ? -127 : (ef - 127) - ((bits & 0x7FFFFFu) > 0x600000u ? 7 : 8);
+    if (k < -127) k = -127;
+    const bool zero = amax == 0.0f;
+    if ((v & 3) == 0) e[v >> 2] = zero ? (uint8_t)0 : (uint8_t)(k + 127);
+    const float r = __uint_as_float((uint32_t)(127 - k) << 23);   // 2^-k, k in [-127, 120]
+    u32x2 o = {0u, 0u};
+    if (!zero) {
+        o[0] = pack_e4m3x4(bf16_lo(w[0]) * r, bf16_hi(w[0]) * r, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r);
+        o[1] = pack_e4m3x4(bf16_lo(w[2]) * r, bf16_hi(w[2]) * r, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r);
+    }
+    __builtin_nontemporal_store(o, q + v);
+}
+
+__global__ void __launch_bounds__(256)
+mxq_1x32_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, uint8_t *__restrict__ e,
+                uint64_t npack) {
+    const uint64_t stride = (uint64_t)gridDim.x * 256;
+    // every lane of a 4-lane block group has the same v0 < npack and
+    // v1 < npack: npack and the stride are multiples of 4
+    for (uint64_t v0 = (uint64_t)blockIdx.x * 256 + threadIdx.x; v0 < npack; v0 += 2 * stride) {
+        const uint64_t v1 = v0 + stride;
+        const bool l1 = v1 < npack;
+        const u32x4 w0 = __builtin_nontemporal_load(x + v0);
+        u32x4 w1 = {0u, 0u, 0u, 0u};
+        if (l1) w1 = __builtin_nontemporal_load(x + v1);
+        mxq_pack(w0, q, e, v0, true);
+        mxq_pack(w1, q, e, v1, l1);
+    }
+}
+
 unsigned grid_rows(int64_t rows) { return (unsigned)(rows < 1048576 ? (rows > 0 ? rows : 1) : 1048576); }
 
 }  // namespace
@@ -420,4 +469,14 @@ int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, in
     if (blocks < 1) blocks = 1;
     return bs_enqueue(actq_1x128_kernel, dim3((unsigned)blocks), dim3(256), stream, (const u32x4 *)x,
                       (u32x4 *)q, scale, npair);
+}
+
+int bs_launch_mxq(const uint16_t *x, uint8_t *q, uint8_t *e, int64_t rows, int64_t cols,
+                  hipStream_t stream) {
+    const uint64_t npack = (uint64_t)rows * (uint64_t)(cols / 8);
+    uint64_t blocks = (npack + 511) / 512;
+    if (blocks > 1048576) blocks = 1048576;
+    if (blocks < 1) blocks = 1;
+    return bs_enqueue(mxq_1x32_kernel, dim3((unsigned)blocks), dim3(256), stream, (const u32x4 *)x,
+                      (u32x2 *)q, e, npack);
 }

@@ -11,6 +11,9 @@
  *                activation/weight quantizer that produces bsgemm_fp8's input)
  *   actq_e4m3    bf16 activation -> e4m3 codes + fp32 1x128 scales (the
  *                on-GPU step before bsgemm_fp8 when the layer input is bf16)
+ *   mxgemm_fp8   the mxfp8 variant of the GEMM: e4m3 operands with E8M0 scales
+ *                per 1x32 block on both A and B, applied by the MFMA
+ *   mxq_e4m3     bf16 -> e4m3 codes + E8M0 1x32 scales (mxgemm_fp8's operands)
  *
  * Pages defining the operations (cited by title and section):
  *   [PR40757] sglang PR 40757 "[AMD][gfx950] DSV4: fuse wo_b's GEMM with its
@@ -18,9 +21,13 @@
  *             by an all-reduce of [M, hidden]; each destination's row band
  *             written as its own unit), "Numbers" (fused and unfused agree up
  *             to accumulation order).
- *   [PR43480] sglang PR 43480 (DeepSeek-V4.1-Flash wo_b): "Numerics,
- *             measured where the path engages" (on the aiter route wo_b is
- *             handed a plain bf16 activation and quantises it itself).
+ *   [PR43480] sglang PR 43480 (DeepSeek-V4.1-Flash wo_b): "What" (an mxfp8
+ *             GEMM followed by the all-reduce), "Not in this PR" (V4.1-Flash
+ *             quantises at 32-wide ue8m0), "Numerics, measured where the path
+ *             engages" (on the aiter route wo_b is handed a plain bf16
+ *             activation and quantises it itself); the review reply on the
+ *             duplicated ue8m0 scale rule (exponent from the IEEE bits, exact
+ *             at powers of two).
  *   [MORI]    "MORI GEMM + All-Reduce Benchmark": "Running the benchmark"
  *             (--quant blockscale: A per 1x128, B per 128x128, fp32 scales;
  *             shape [M,7168], K=2048), "Where the time goes" (reduce /
@@ -191,6 +198,45 @@ bs_status blockq_e4m3(const float *x, uint8_t *q, float *scale,
  */
 bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
                     int64_t rows, int64_t cols, void *stream);
+
+/*
+ * mxfp8 GEMM, the variant of [PR43480] "What" / "Not in this PR": C = A * B^T
+ * with A [M,K] e4m3 and a_scale [M, K/32] E8M0 bytes (one per 1x32 block of
+ * a row; value 2^(byte - 127)), B [N,K] e4m3 and b_scale [N, K/32] E8M0
+ * bytes, fp32 accumulation, bf16 output, written in the same destination-major
+ * bands as bsgemm_fp8 (bands, band_stride as there).  The block scales are
+ * applied by gfx950's scaled MFMA; the sum is accumulated over K in fp32 in
+ * the instruction's own order, so results are compared with the exact product
+ * at a relL2 tolerance.
+ *
+ * Requirements: M >= 0; N > 0, N % 128 == 0; K > 0, K % 128 == 0, K <= 2^22;
+ * bands in [1, 64] dividing M; band_stride 0 or >= (M/bands)*N and a multiple
+ * of 8; A, B, C 16-byte aligned; a_scale, b_scale 4-byte aligned; C must not
+ * overlap an input.
+ */
+bs_status mxgemm_fp8(const uint8_t *A, const uint8_t *a_scale,
+                     const uint8_t *B, const uint8_t *b_scale,
+                     uint16_t *C, int64_t M, int64_t N, int64_t K,
+                     int32_t bands, int64_t band_stride, void *stream);
+
+/*
+ * mxfp8 operand quantizer ([PR43480] "Not in this PR": 32-wide ue8m0; the
+ * review reply on the ue8m0 scale rule: exponent from the IEEE bits, exact at
+ * powers of two).  For each block of 32 consecutive elements of a row:
+ * amax = max |x|; the scale is 2^k with k the smallest integer such that
+ * amax <= 448 * 2^k (clamped below at -127); scale byte = k + 127; codes =
+ * e4m3 round-to-nearest-even of x * 2^-k (never saturating).  A zero block
+ * gets scale byte 0 and codes 0x00.
+ *
+ *   x      bf16 [rows, cols] (finite)
+ *   q      e4m3 [rows, cols]
+ *   scale  E8M0 bytes [rows, cols/32]
+ *
+ * Requirements: rows >= 0; cols > 0, cols % 32 == 0; x, q 16-byte aligned; no
+ * output overlaps x or the other output.
+ */
+bs_status mxq_e4m3(const uint16_t *x, uint8_t *q, uint8_t *scale,
+                   int64_t rows, int64_t cols, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *bs_status_str(bs_status status);

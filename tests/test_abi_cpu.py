@@ -118,3 +118,36 @@ def test_actq_rejections(L):
     assert f(P, P + 1024, P + 0x200000, 4, 256, None) == INV                 # q overlaps x (2 KiB)
     assert f(P, P + 0x100000, P + 0x100000 + 512, 4, 256, None) == INV       # scale overlaps q
     assert f(P, P + 0x100000, P + 0x200000, 0, 256, None) == OK
+
+
+def mxgemm(L, A=P, sa=P + 0x100000, B=P + 0x200000, sb=P + 0x300000, C=P + 0x1000000,
+           M=256, N=512, K=256, bands=1, stride=0):
+    return L.mxgemm_fp8(A, sa, B, sb, C, M, N, K, bands, stride, None)
+
+
+def test_mxgemm_rejections(L):
+    assert mxgemm(L, A=0) == INV and mxgemm(L, sa=0) == INV and mxgemm(L, sb=0) == INV
+    assert mxgemm(L, C=0) == INV and mxgemm(L, M=-1) == INV and mxgemm(L, N=0) == INV
+    assert mxgemm(L, K=0) == INV and mxgemm(L, bands=0) == INV and mxgemm(L, stride=-8) == INV
+    assert mxgemm(L, N=500) == UNS and mxgemm(L, K=160) == UNS            # K % 128
+    assert mxgemm(L, bands=65) == UNS and mxgemm(L, M=250, bands=8) == UNS
+    assert mxgemm(L, bands=2, stride=128 * 512 - 8) == UNS
+    assert mxgemm(L, A=P + 8) == UNS and mxgemm(L, C=P + 0x1000002) == UNS
+    assert mxgemm(L, sa=P + 0x100002) == UNS and mxgemm(L, sb=P + 0x300001) == UNS
+    assert mxgemm(L, K=1 << 23) == UNS
+    assert mxgemm(L, C=P + 1024) == INV                                     # C over A
+    assert mxgemm(L, C=P + 0x300000 + 64) == INV                           # C over b_scale
+    assert mxgemm(L, M=0) == OK
+
+
+def test_mxq_rejections(L):
+    f = L.mxq_e4m3
+    assert f(0, P + 0x100000, P + 0x200000, 4, 256, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, -1, 256, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, 4, 0, None) == INV
+    assert f(P, P + 0x100000, P + 0x200000, 4, 48, None) == UNS              # cols % 32
+    assert f(P + 8, P + 0x100000, P + 0x200000, 4, 256, None) == UNS         # x alignment
+    assert f(P, P + 0x100008, P + 0x200000, 4, 256, None) == UNS             # q alignment
+    assert f(P, P + 1024, P + 0x200000, 4, 256, None) == INV                 # q overlaps x (2 KiB)
+    assert f(P, P + 0x100000, P + 0x100000 + 512, 4, 256, None) == INV       # scale overlaps q
+    assert f(P, P + 0x100000, P + 0x200001, 0, 256, None) == OK              # scales: byte aligned
