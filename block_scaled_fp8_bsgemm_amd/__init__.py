@@ -12,6 +12,8 @@ library has not been built, importing the functions raises immediately.
   rowdq_e4m3(q, scale, y=None)
   blockq_e4m3(x, block_rows, q=None, scale=None)
   actq_e4m3(x, q=None, scale=None)
+  bprepack_e4m3(B, Bp=None)
+  bsgemm_fp8_pb(A, a_scale, Bp, b_scale, C=None, bands=1, band_stride=0)
   mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0)
   mxq_e4m3(x, q=None, scale=None)
 
@@ -29,7 +31,7 @@ BS_OK, BS_ERR_INVALID, BS_ERR_UNSUPPORTED, BS_ERR_LAUNCH = 0, 1, 2, 3
 
 # every extern "C" symbol of include/bsgemm.h
 EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
-           "mxgemm_fp8", "mxq_e4m3", "bs_status_str")
+           "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb", "bs_status_str")
 
 _lib = None
 
@@ -57,8 +59,10 @@ def load():
     L.actq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
     L.mxgemm_fp8.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp]
     L.mxq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
+    L.bprepack_e4m3.argtypes = [vp, vp, i64, i64, vp]
+    L.bsgemm_fp8_pb.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp]
     for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
-              "mxgemm_fp8", "mxq_e4m3"):
+              "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb"):
         getattr(L, f).restype = ctypes.c_int
     L.bs_status_str.argtypes = [ctypes.c_int]
     L.bs_status_str.restype = ctypes.c_char_p
@@ -230,3 +234,33 @@ def mxq_e4m3(x, q=None, scale=None, stream=None):
                          rows, cols, _stream(stream))
     _check(st, "mxq_e4m3")
     return q, scale
+
+
+def bprepack_e4m3(B, Bp=None, stream=None):
+    """Bp (uint8, N*K bytes) = the weight B [N,K] e4m3 in bsgemm_fp8_pb's operand order."""
+    torch = _torch()
+    N, K = B.shape
+    if Bp is None:
+        Bp = torch.empty(N * K, dtype=torch.uint8, device=B.device)
+    st = load().bprepack_e4m3(_ptr(B, _u8(), "B"), _ptr(Bp, _u8(), "Bp"), N, K, _stream(stream))
+    _check(st, "bprepack_e4m3")
+    return Bp
+
+
+def bsgemm_fp8_pb(A, a_scale, Bp, b_scale, C=None, bands=1, band_stride=0, stream=None):
+    """bsgemm_fp8 with the weight prepacked by bprepack_e4m3 (Bp holds N*K bytes; N is
+    taken from b_scale, [N/128, K/128])."""
+    torch = _torch()
+    M, K = A.shape
+    N = b_scale.shape[0] * 128
+    if Bp.numel() != N * K:
+        raise ValueError(f"Bp must hold N*K = {N * K} bytes, got {Bp.numel()}")
+    if C is None:
+        band_rows = M // bands if bands > 0 else 0
+        stride = band_stride if band_stride else band_rows * N
+        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+    st = load().bsgemm_fp8_pb(_ptr(A, _u8(), "A"), _ptr(a_scale, _f32(), "a_scale"),
+                              _ptr(Bp, _u8(), "Bp"), _ptr(b_scale, _f32(), "b_scale"),
+                              _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
+    _check(st, "bsgemm_fp8_pb")
+    return C

@@ -42,9 +42,20 @@ const char *bs_status_str(bs_status status) {
     return "unknown status";
 }
 
-bs_status bsgemm_fp8(const uint8_t *A, const float *a_scale, const uint8_t *B, const float *b_scale,
-                     uint16_t *C, int64_t M, int64_t N, int64_t K, int32_t bands,
-                     int64_t band_stride, void *stream) {
+}  // extern "C"
+
+namespace {
+
+typedef int (*blockscale_launch)(const uint8_t *, const float *, const uint8_t *, const float *,
+                                 uint16_t *, int64_t, int64_t, int64_t, int64_t, int64_t,
+                                 hipStream_t);
+
+// Validation shared by the two blockscale GEMM entry points: B is either the
+// weight [N, K] row-major or its prepacked form, the same N * K bytes.
+bs_status blockscale_gemm(blockscale_launch launch, const uint8_t *A, const float *a_scale,
+                          const uint8_t *B, const float *b_scale, uint16_t *C, int64_t M,
+                          int64_t N, int64_t K, int32_t bands, int64_t band_stride,
+                          void *stream) {
     if (!A || !a_scale || !B || !b_scale || !C) return BS_ERR_INVALID;
     if (M < 0 || N <= 0 || K <= 0 || bands < 1 || band_stride < 0) return BS_ERR_INVALID;
     if (N % 128 || K % 128 || bands > 64) return BS_ERR_UNSUPPORTED;
@@ -62,10 +73,36 @@ bs_status bsgemm_fp8(const uint8_t *A, const float *a_scale, const uint8_t *B, c
         overlap(rc, range_of(a_scale, M * KB * 4)) || overlap(rc, range_of(b_scale, NB * KB * 4)))
         return BS_ERR_INVALID;
     if (M == 0) return BS_OK;
-    return bs_launch_gemm(A, a_scale, B, b_scale, C, M, N, K, band_rows == 0 ? 1 : band_rows,
-                          stride, as_stream(stream)) == 0
+    return launch(A, a_scale, B, b_scale, C, M, N, K, band_rows == 0 ? 1 : band_rows, stride,
+                  as_stream(stream)) == 0
                ? BS_OK
                : BS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+bs_status bsgemm_fp8(const uint8_t *A, const float *a_scale, const uint8_t *B, const float *b_scale,
+                     uint16_t *C, int64_t M, int64_t N, int64_t K, int32_t bands,
+                     int64_t band_stride, void *stream) {
+    return blockscale_gemm(bs_launch_gemm, A, a_scale, B, b_scale, C, M, N, K, bands, band_stride,
+                           stream);
+}
+
+bs_status bsgemm_fp8_pb(const uint8_t *A, const float *a_scale, const uint8_t *Bp,
+                        const float *b_scale, uint16_t *C, int64_t M, int64_t N, int64_t K,
+                        int32_t bands, int64_t band_stride, void *stream) {
+    return blockscale_gemm(bs_launch_gemm_pb, A, a_scale, Bp, b_scale, C, M, N, K, bands,
+                           band_stride, stream);
+}
+
+bs_status bprepack_e4m3(const uint8_t *B, uint8_t *Bp, int64_t N, int64_t K, void *stream) {
+    if (!B || !Bp || N <= 0 || K <= 0) return BS_ERR_INVALID;
+    if (N % 128 || K % 128 || N >= kMaxDim || K > kMaxK) return BS_ERR_UNSUPPORTED;
+    if (!aligned(B, 16) || !aligned(Bp, 16)) return BS_ERR_UNSUPPORTED;
+    if (overlap(range_of(B, N * K), range_of(Bp, N * K))) return BS_ERR_INVALID;
+    return bs_launch_bprepack(B, Bp, N, K, as_stream(stream)) == 0 ? BS_OK : BS_ERR_LAUNCH;
 }
 
 bs_status mxgemm_fp8(const uint8_t *A, const uint8_t *a_scale, const uint8_t *B, const uint8_t *b_scale,

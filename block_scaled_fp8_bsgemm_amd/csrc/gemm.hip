@@ -102,6 +102,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, in
 struct Loader {
     __amdgpu_buffer_rsrc_t rA, rB, rS;   // rS: a_scale (waves 0..3) or b_scale (4..7)
     __amdgpu_buffer_rsrc_t rZ;           // zero-size: every load through it reads nothing
+    int poff;    // prepacked B: this lane's byte offset in its wave's first fragment
+    int pstep;   // prepacked B: bytes from one 16-row group to the next (K/128 * 2 KiB)
     int voff;    // this lane's byte offset of its chunk in the A / B row panels
     int k8;      // 8 rows of a panel, in bytes
     int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
@@ -292,6 +294,103 @@ __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[
     a = a_next;
 }
 
+// ---- blockscale with prepacked B -----------------------------------------
+// The prepacked weight holds, for each 16-row group of B and K block, the
+// 2 KiB the MFMA takes as its B operand, in lane order and split in two
+// 1 KiB halves: half h, lane l = 16 g + r: bytes [32 g + 16 h, 32 g + 16 h + 16)
+// of row r's 128-byte K segment.  A wave loads its fragment j of block kb
+// straight into registers with two fully coalesced 1 KiB loads; B needs no
+// LDS and no DMA.  A block past the end loads through the zero-size
+// descriptor.
+template <int H>
+__device__ __forceinline__ void load_bp_half(const Loader &L, v8i &f, int j, int kb, bool valid) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(valid ? L.rB : L.rZ, L.poff + H * 1024,
+                                                          j * L.pstep + kb * 2048, 0);
+#pragma unroll
+    for (int e = 0; e < 4; e++) f[4 * H + e] = (int)v[e];
+}
+
+// The loads of block kb + 1 during the first MFMAs of block kb: the B
+// fragments into the registers block kb - 1 used, the A slots and scales by
+// DMA into the other stage (unread since the previous block's barrier).
+template <int ST>
+__device__ __forceinline__ void load_next_pb(const Loader &L, v8i (&bn)[TN], int k, int kb,
+                                             int KB) {
+    const bool v = kb + 1 < KB;
+    if (k < 8) {
+        if (k & 1) load_bp_half<1>(L, bn[k >> 1], k >> 1, kb + 1, v);
+        else load_bp_half<0>(L, bn[k >> 1], k >> 1, kb + 1, v);
+    }
+    if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
+    if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
+    if (k == 2) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
+    if (k == 3) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
+    if (k == 4) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
+}
+
+// The first K block of a tile: A slots and scales by DMA into stage ST, the
+// B fragments into b; then the head reads (A row group 0, the scales).
+template <int ST>
+__device__ __forceinline__ void load_first_pb(const Loader &L, v8i (&b)[TN]) {
+    dma_piece<ST, 8>(L, 0, true);
+    dma_piece<ST, 0>(L, 0, true); dma_piece<ST, 2>(L, 0, true);
+    dma_piece<ST, 4>(L, 0, true); dma_piece<ST, 6>(L, 0, true);
+#pragma unroll
+    for (int j = 0; j < TN; j++) {
+        load_bp_half<0>(L, b[j], j, 0, true);
+        load_bp_half<1>(L, b[j], j, 0, true);
+    }
+}
+
+template <int ST>
+__device__ __forceinline__ void read_head_pb(v8i &a, float (&s)[TM], int wm, int wn, int frow,
+                                             int fc) {
+    a = lds_frag(stA<ST>(), wm * WM + frow, fc);
+    RawScales r;
+    read_scales<ST>(r, wm, wn, frow);
+    combine_scales(s, r);
+}
+
+// One K block as kblock below, with the B fragments of this block in bc and
+// those of the next block loaded into bn.
+template <int ST>
+__device__ __forceinline__ void kblock_pb(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
+                                          const v8i (&bc)[TN], v8i (&bn)[TN], float (&s)[TM],
+                                          const Loader &L, int kb, int KB, int wm, int wn,
+                                          int frow, int fc) {
+    const uint8_t *as = stA<ST>();
+    v8i an = a;
+    v8i a_next = a;
+    RawScales rn;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const v8i af = an;
+        if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
+        if (i == TM - 1) {
+            wait_dma_and_sync();
+            a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
+            read_scales<ST ^ 1>(rn, wm, wn, frow);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int k = i * TN + j;
+            p[k & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bc[j], af, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            if (k >= 3) {
+                const int kp = k - 3;
+                fold4(acc[kp / TN][kp % TN], p[kp & 3], s[kp / TN]);
+            } else {
+                fold4(acc[TM - 1][k + 1], p[(k + 1) & 3], s_tail);
+            }
+            load_next_pb<ST>(L, bn, k, kb, KB);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    s_tail = s[TM - 1];
+    combine_scales(s, rn);
+    a = a_next;
+}
+
 // One K block from stage ST: 8 x 4 MFMAs per wave, each into a zeroed
 // temporary p[k % 4] that is folded into its accumulator (one fma per
 // element, by the row's combined scale) three MFMAs later, when it is
@@ -361,9 +460,12 @@ __device__ __forceinline__ uint8_t *out_row(int ml) {
     return base + (ml & 63) * (BN * 2);
 }
 
-// One 256x256 output tile; MX selects the mxfp8 operands (E8M0 scales per
-// 1x32 block, applied by the scaled MFMA) instead of the blockscale ones.
-template <bool MX>
+// One 256x256 output tile.  MODE_BS: blockscale operands, A and B staged in
+// LDS; MODE_PB: blockscale with the prepacked B loaded into registers;
+// MODE_MX: mxfp8 operands (E8M0 scales per 1x32 block, applied by the scaled
+// MFMA).
+constexpr int MODE_BS = 0, MODE_PB = 1, MODE_MX = 2;
+template <int MODE>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     // ---- workgroup -> tile (XCD-aware, grouped) ----
     const int T = g.tiles_m * g.tiles_n;
@@ -390,6 +492,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     L.rA = make_rsrc(g.A + m0 * K, (g.M - m0) * K);
     L.rB = make_rsrc(g.B + n0 * K, (g.N - n0) * K);
     const int KQ = (int)(K / 32);   // mxfp8 scale bytes per row
+    constexpr bool MX = MODE == MODE_MX;
+    if (MODE == MODE_PB) {
+        L.pstep = KB * 2048;
+        L.rB = make_rsrc(g.B + (n0 / 16) * (int64_t)L.pstep, (g.N - n0) * K);
+        L.poff = wn * TN * L.pstep + lane * 16;
+    }
     if (MX) {
         L.rS = wave < 4 ? make_rsrc((const uint8_t *)g.sa + m0 * KQ, (g.M - m0) * KQ)
                         : make_rsrc((const uint8_t *)g.sb + n0 * KQ, (g.N - n0) * KQ);
@@ -418,7 +526,35 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
 #pragma unroll
         for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (MX) {
+    if constexpr (MODE == MODE_PB) {
+        // stage 1 runs with the B registers bA, stage 0 with bB
+        v8i a, bA[TN], bB[TN];
+        float s[TM];
+        if (KB & 1) {
+            load_first_pb<0>(L, bB);
+            wait_dma_and_sync();
+            read_head_pb<0>(a, s, wm, wn, frow, fc);
+        } else {
+            load_first_pb<1>(L, bA);
+            wait_dma_and_sync();
+            read_head_pb<1>(a, s, wm, wn, frow, fc);
+        }
+        v4f p[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+        float s_tail = 0.f;
+        int kb = 0;
+        if (KB & 1) {
+            kblock_pb<0>(acc, p, s_tail, a, bB, bA, s, L, 0, KB, wm, wn, frow, fc);
+            kb = 1;
+        }
+        for (; kb < KB; kb += 2) {
+            kblock_pb<1>(acc, p, s_tail, a, bA, bB, s, L, kb, KB, wm, wn, frow, fc);
+            kblock_pb<0>(acc, p, s_tail, a, bB, bA, s, L, kb + 1, KB, wm, wn, frow, fc);
+        }
+#pragma unroll
+        for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
+    } else if constexpr (MX) {
         const int gq = lane >> 4;
         v8i a, bf[TN];
         MxScales x;
@@ -511,9 +647,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     }
 }
 
-__global__ void __launch_bounds__(NTHREADS) bsgemm_tile_kernel(GemmArgs g) { gemm_tile<false>(g); }
+__global__ void __launch_bounds__(NTHREADS) bsgemm_tile_kernel(GemmArgs g) { gemm_tile<MODE_BS>(g); }
 
-__global__ void __launch_bounds__(NTHREADS) mxgemm_tile_kernel(GemmArgs g) { gemm_tile<true>(g); }
+__global__ void __launch_bounds__(NTHREADS) bsgemm_pb_tile_kernel(GemmArgs g) { gemm_tile<MODE_PB>(g); }
+
+__global__ void __launch_bounds__(NTHREADS) mxgemm_tile_kernel(GemmArgs g) { gemm_tile<MODE_MX>(g); }
+
+// B [N, K] -> the prepacked layout [N/16][K/128][2][64][16 B]: unit u of the
+// output (16 bytes) is half h, lane l = 16 g + r of 16-row group nt and K
+// block kb, and holds bytes [32 g + 16 h, +16) of row 16 nt + r's K block kb.
+// One lane per output unit: the writes are contiguous, the reads 16-byte
+// aligned gathers.
+__global__ void __launch_bounds__(256)
+bprepack_kernel(const u32x4 *__restrict__ B, u32x4 *__restrict__ Bp, int64_t units, int64_t K) {
+    const int64_t KB = K / 128;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units;
+         u += (int64_t)gridDim.x * 256) {
+        const int l = (int)(u & 63);
+        const int h = (int)((u >> 6) & 1);
+        const int64_t blk = u >> 7;          // nt * KB + kb
+        const int64_t nt = blk / KB, kb = blk - nt * KB;
+        const int64_t row = nt * 16 + (l & 15);
+        const int64_t col = kb * 128 + 32 * (l >> 4) + 16 * h;
+        Bp[u] = B[(row * K + col) >> 4];
+    }
+}
 
 }  // namespace
 
@@ -541,6 +699,21 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
                    int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
     return bs_enqueue(bsgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
+}
+
+int bs_launch_gemm_pb(const uint8_t *A, const float *sa, const uint8_t *Bp, const float *sb,
+                      uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                      int64_t band_stride, hipStream_t stream) {
+    const GemmArgs g = gemm_args(A, sa, Bp, sb, C, M, N, K, band_rows, band_stride);
+    return bs_enqueue(bsgemm_pb_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
+}
+
+int bs_launch_bprepack(const uint8_t *B, uint8_t *Bp, int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t units = N * K / 16;
+    int64_t blocks = (units + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return bs_enqueue(bprepack_kernel, dim3((unsigned)blocks), dim3(256), stream, (const u32x4 *)B,
+                      (u32x4 *)Bp, units, K);
 }
 
 int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, const uint8_t *sb,

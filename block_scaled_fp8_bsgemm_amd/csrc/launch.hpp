@@ -8,6 +8,10 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
                    uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                    int64_t band_stride, hipStream_t stream);
 
+int bs_launch_gemm_pb(const uint8_t *A, const float *sa, const uint8_t *Bp, const float *sb,
+                      uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
+                      int64_t band_stride, hipStream_t stream);
+int bs_launch_bprepack(const uint8_t *B, uint8_t *Bp, int64_t N, int64_t K, hipStream_t stream);
 int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, const uint8_t *sb,
                      uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                      int64_t band_stride, hipStream_t stream);

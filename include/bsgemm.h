@@ -11,6 +11,9 @@
  *                activation/weight quantizer that produces bsgemm_fp8's input)
  *   actq_e4m3    bf16 activation -> e4m3 codes + fp32 1x128 scales (the
  *                on-GPU step before bsgemm_fp8 when the layer input is bf16)
+ *   bprepack_e4m3  one-time rearrangement of the weight B into the GEMM's
+ *                operand order (load-time weight preparation)
+ *   bsgemm_fp8_pb  the GEMM reading B in that prepacked form
  *   mxgemm_fp8   the mxfp8 variant of the GEMM: e4m3 operands with E8M0 scales
  *                per 1x32 block on both A and B, applied by the MFMA
  *   mxq_e4m3     bf16 -> e4m3 codes + E8M0 1x32 scales (mxgemm_fp8's operands)
@@ -25,9 +28,14 @@
  *             GEMM followed by the all-reduce), "Not in this PR" (V4.1-Flash
  *             quantises at 32-wide ue8m0), "Numerics, measured where the path
  *             engages" (on the aiter route wo_b is handed a plain bf16
- *             activation and quantises it itself); the review reply on the
- *             duplicated ue8m0 scale rule (exponent from the IEEE bits, exact
- *             at powers of two).
+ *             activation and quantises it itself); "Worth a reviewer's
+ *             attention" (the native gfx950 route rebinds the weight to a
+ *             shuffled [N/16, K/128, 2048] layout, and reading one layout as
+ *             the other gives an uncorrelated result instead of an error);
+ *             the review reply on the duplicated ue8m0 scale rule (exponent
+ *             from the IEEE bits, exact at powers of two) and the one on the
+ *             lazy second copy of the weight (weight preparation moved to
+ *             load time).
  *   [MORI]    "MORI GEMM + All-Reduce Benchmark": "Running the benchmark"
  *             (--quant blockscale: A per 1x128, B per 128x128, fp32 scales;
  *             shape [M,7168], K=2048), "Where the time goes" (reduce /
@@ -198,6 +206,46 @@ bs_status blockq_e4m3(const float *x, uint8_t *q, float *scale,
  */
 bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
                     int64_t rows, int64_t cols, void *stream);
+
+/*
+ * Prepacks the weight B for bsgemm_fp8_pb: a one-time rearrangement done when
+ * the weight is loaded ([PR43480], the review reply on the lazy second copy
+ * of the weight; [PR40757] "What": the fused path serves only a weight that
+ * was preshuffled at load).  Bp holds the same N*K bytes as B in the order
+ * the GEMM's MFMA consumes them:
+ *
+ *   Bp[((nt * (K/128) + kb) * 2 + h) * 1024 + (16 g + r) * 16 + e]
+ *       = B[16 nt + r, 128 kb + 32 g + 16 h + e]
+ *
+ * for 16-row group nt, K block kb, half h in {0,1}, g in [0,4), r in [0,16),
+ * e in [0,16): each 2 KiB block is one 16 x 128 tile of B, laid out as the
+ * 64 lanes' operand bytes.  The layout is a contract between this call and
+ * bsgemm_fp8_pb only; nothing infers it from a shape ([PR43480] "Worth a
+ * reviewer's attention": one layout read as the other gives garbage, not an
+ * error).
+ *
+ *   B   e4m3 [N, K] row-major (the weight as stored, [out, in])
+ *   Bp  e4m3, N*K bytes, prepacked (caller-owned, written here)
+ *
+ * Requirements: N > 0, N % 128 == 0; K > 0, K % 128 == 0, K <= 2^22; B and Bp
+ * 16-byte aligned and not overlapping (no in-place prepack).
+ */
+bs_status bprepack_e4m3(const uint8_t *B, uint8_t *Bp, int64_t N, int64_t K,
+                        void *stream);
+
+/*
+ * bsgemm_fp8 with the weight in the prepacked form bprepack_e4m3 writes: the
+ * same operation, arguments, requirements, errors and results (bit for bit)
+ * as bsgemm_fp8, except that B is replaced by Bp.  The kernel loads each
+ * wave's B operands straight from Bp into registers (fully coalesced 1 KiB
+ * loads), so B takes no LDS staging; A and the scales are staged as in
+ * bsgemm_fp8.  Passing an unpacked B here (or Bp to bsgemm_fp8) is not
+ * detected and gives a wrong result.
+ */
+bs_status bsgemm_fp8_pb(const uint8_t *A, const float *a_scale,
+                        const uint8_t *Bp, const float *b_scale,
+                        uint16_t *C, int64_t M, int64_t N, int64_t K,
+                        int32_t bands, int64_t band_stride, void *stream);
 
 /*
  * mxfp8 GEMM, the variant of [PR43480] "What" / "Not in this PR": C = A * B^T

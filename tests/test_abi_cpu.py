@@ -151,3 +151,31 @@ def test_mxq_rejections(L):
     assert f(P, P + 1024, P + 0x200000, 4, 256, None) == INV                 # q overlaps x (2 KiB)
     assert f(P, P + 0x100000, P + 0x100000 + 512, 4, 256, None) == INV       # scale overlaps q
     assert f(P, P + 0x100000, P + 0x200001, 0, 256, None) == OK              # scales: byte aligned
+
+
+def test_gemm_pb_rejections(L):
+    def g(**kw):
+        a = dict(A=P, sa=P + 0x100000, B=P + 0x200000, sb=P + 0x300000, C=P + 0x1000000,
+                 M=256, N=512, K=256, bands=1, stride=0)
+        a.update(kw)
+        return L.bsgemm_fp8_pb(a["A"], a["sa"], a["B"], a["sb"], a["C"], a["M"], a["N"], a["K"],
+                               a["bands"], a["stride"], None)
+    assert g(B=0) == INV and g(M=-1) == INV and g(bands=0) == INV
+    assert g(N=500) == UNS and g(K=200) == UNS and g(M=250, bands=8) == UNS
+    assert g(B=P + 0x200008) == UNS and g(sb=P + 0x300002) == UNS
+    assert g(C=P + 0x200000 + 4096) == INV                  # C over the prepacked weight
+    assert g(M=0) == OK
+
+
+def test_bprepack_rejections(L):
+    f = L.bprepack_e4m3
+    assert f(0, P + 0x100000, 512, 256, None) == INV
+    assert f(P, 0, 512, 256, None) == INV
+    assert f(P, P + 0x100000, 0, 256, None) == INV and f(P, P + 0x100000, 512, -128, None) == INV
+    assert f(P, P + 0x100000, 500, 256, None) == UNS                      # N % 128
+    assert f(P, P + 0x100000, 512, 200, None) == UNS                      # K % 128
+    assert f(P, P + 0x100000, 512, 1 << 23, None) == UNS
+    assert f(P + 8, P + 0x100000, 512, 256, None) == UNS                  # alignment
+    assert f(P, P + 0x100008, 512, 256, None) == UNS
+    assert f(P, P, 512, 256, None) == INV                                 # in place
+    assert f(P, P + 512 * 256 - 16, 512, 256, None) == INV               # overlapping

@@ -1,0 +1,56 @@
+"""Pins for O12, the prepacked weight layout: a bijection of the N*K bytes
+in which every 2 KiB block is one whole 16-row x 128-column tile of B, the
+blocks ordered by row group then K block, each block's two 1 KiB halves
+splitting every 32-byte lane segment in its first and second 16 bytes, and
+the lanes of a half ordered lane group first (16 K-consecutive rows per
+group).  The device GEMM on prepacked B equalling the plain one bit for bit is
+the remaining check (GPU tests)."""
+import numpy as np
+
+import oracle
+
+
+def ids(N, K):
+    return np.arange(N * K, dtype=np.int64).reshape(N, K)
+
+
+def test_prepack_is_a_bijection():
+    N, K = 256, 512
+    out = oracle.bprepack(ids(N, K))
+    assert out.size == N * K
+    assert np.array_equal(np.sort(out), np.arange(N * K))
+
+
+def test_prepack_blocks_are_whole_tiles_in_order():
+    N, K = 64, 384
+    KB = K // 128
+    out = oracle.bprepack(ids(N, K)).reshape(-1, 2048)
+    assert out.shape[0] == (N // 16) * KB
+    for b in range(out.shape[0]):
+        nt, kb = divmod(b, KB)
+        rows, cols = np.divmod(out[b], K)
+        assert set(rows) == set(range(16 * nt, 16 * nt + 16))
+        assert set(cols) == set(range(128 * kb, 128 * kb + 128))
+
+
+def test_prepack_lane_segments():
+    """Lane l of a block reads, over its two halves, 32 consecutive bytes of one
+    row: row 16 nt + l % 16, columns 32 (l / 16) .. +32 of the K block (the
+    unscaled 16x16x128 MFMA's operand: lane group g holds K [32g, 32g+32))."""
+    N, K = 32, 256
+    B = ids(N, K)
+    out = oracle.bprepack(B).reshape(N // 16, K // 128, 2, 64, 16)
+    rng = np.random.default_rng(0)
+    for _ in range(64):
+        nt, kb, l = rng.integers(0, N // 16), rng.integers(0, K // 128), rng.integers(0, 64)
+        seg = np.concatenate([out[nt, kb, 0, l], out[nt, kb, 1, l]])
+        r, g = 16 * nt + l % 16, l // 16
+        assert np.array_equal(seg, B[r, 128 * kb + 32 * g: 128 * kb + 32 * g + 32])
+
+
+def test_prepack_of_uint8_weight():
+    rng = np.random.default_rng(1)
+    B = rng.integers(0, 256, size=(128, 256), dtype=np.uint8)
+    out = oracle.bprepack(B)
+    assert out.dtype == np.uint8 and out.size == B.size
+    assert np.array_equal(np.sort(out), np.sort(B.ravel()))
