@@ -31,6 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
 PAGES_STEP_US = 438.2 + 42.5 + 11.8 + 61.0   # gemm+reduce+quantize+dequantize, fp8/sdma column
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bsgemm_m16384_traffic.json")
+HOST_LEAD_CYCLES = 4_000_000  # spin-kernel cycles (~2 ms) queued ahead of a timed loop
 
 
 def kernel_hash():
@@ -117,6 +118,10 @@ def streaming_rates(M, N, P, dev, iters=20):
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # a ~1 ms spin ahead of the first event lets the host queue every
+        # timed call before the GPU reaches it, so the events see the kernels
+        # back to back and not the Python call overhead between them
+        torch.cuda._sleep(HOST_LEAD_CYCLES)
         e0.record()
         for i in range(iters):
             fn(i % nsets)

@@ -38,43 +38,55 @@ struct PartPtrs {
     const u32x4 *p[16];
 };
 
-// one 16-byte pack (8 bf16) of every part per lane and iteration; the P loads
-// are issued together before the fp32 adds, which run in part order from +0.
+// Flat grid over 16-byte packs (8 bf16): each lane takes two packs 256
+// apart and issues all 2P loads (non-temporal: every part is read once)
+// before the fp32 adds, which run in part order from +0; the outputs are
+// written non-temporally.
+template <int P>
+__device__ __forceinline__ u32x4 reduce_pack(const u32x4 (&w)[P]) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[e] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            acc[2 * e] += bf16_lo(w[p][e]);
+            acc[2 * e + 1] += bf16_hi(w[p][e]);
+        }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; e++) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
+    return o;
+}
+
 template <int P>
 __global__ void __launch_bounds__(256)
 band_reduce_kernel(PartPtrs parts, u32x4 *__restrict__ out, int64_t nvec) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
-        u32x4 w[P];
+    const int64_t stride = (int64_t)gridDim.x * 512;
+    for (int64_t v0 = (int64_t)blockIdx.x * 512 + threadIdx.x; v0 < nvec; v0 += stride) {
+        const int64_t v1 = v0 + 256;
+        const bool two = v1 < nvec;
+        u32x4 w0[P], w1[P];
 #pragma unroll
-        for (int p = 0; p < P; p++) w[p] = __builtin_nontemporal_load(parts.p[p] + v);
-        float acc[8];
+        for (int p = 0; p < P; p++) w0[p] = __builtin_nontemporal_load(parts.p[p] + v0);
+        if (two) {
 #pragma unroll
-        for (int e = 0; e < 8; e++) acc[e] = 0.0f;
-#pragma unroll
-        for (int p = 0; p < P; p++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                acc[2 * e] += bf16_lo(w[p][e]);
-                acc[2 * e + 1] += bf16_hi(w[p][e]);
-            }
+            for (int p = 0; p < P; p++) w1[p] = __builtin_nontemporal_load(parts.p[p] + v1);
         }
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = pack_bf16x2(acc[2 * e], acc[2 * e + 1]);
-        out[v] = o;
+        __builtin_nontemporal_store(reduce_pack<P>(w0), out + v0);
+        if (two) __builtin_nontemporal_store(reduce_pack<P>(w1), out + v1);
     }
 }
 
 template <int P>
 int launch_reduce_p(const PartPtrs &pp, u32x4 *out, int64_t nvec, hipStream_t stream) {
-    int rc = 0;
-    int64_t blocks = (nvec + 255) / 256;
+    int64_t blocks = (nvec + 511) / 512;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    rc |= bs_enqueue(band_reduce_kernel<P>, dim3((unsigned)blocks), dim3(256), stream, pp,
-                       out, nvec);
-    return rc;
+    return bs_enqueue(band_reduce_kernel<P>, dim3((unsigned)blocks), dim3(256), stream, pp, out,
+                      nvec);
 }
 
 // ----------------------------------------------------------- row quantize --
