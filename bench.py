@@ -11,7 +11,8 @@ average time and rate inside the timed steps; `roofline` is the GEMM's
 (measured with HIP events on the launch stream); `streaming` gives the
 HBM-bound kernels measured alone on rotating buffers (>1 GiB, so the 256 MB
 Infinity Cache cannot serve repeats); `mxfp8_gemm` is the mxfp8 variant of the
-GEMM alone at M=16384, N=5120, K=2048; `cpu_baseline` is the CPU oracle timed
+GEMM alone at M=16384, N=5120, K=2048; `pipeline_sweep` gives the step at
+M=8192 and M=20000 (padded to 20096); `cpu_baseline` is the CPU oracle timed
 on a bounded row sample of the same workload and projected to a full step.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
@@ -55,13 +56,16 @@ def load_traffic():
     return t.get("traffic_bytes")
 
 
-def build_inputs(M, N, K, P, dev):
+def build_inputs(M, N, K, P, dev, M_real=None):
+    """GEMM operands for M rows (the first M_real drawn, the rest zero padding),
+    the P-1 stand-in bands and the quantized stand-in wire buffer."""
     import numpy as np
     import torch
     import block_scaled_fp8_bsgemm_amd as bs
     import synth
 
-    A, B = synth.operand_fp32(M, N, K, seed=0, heavy=True)
+    A, B = synth.operand_fp32(M_real or M, N, K, seed=0, heavy=True)
+    A = synth.pad_rows(A, M)
     dA32 = torch.from_numpy(A).to(dev)
     dB32 = torch.from_numpy(B).to(dev)
     qa, sa = bs.blockq_e4m3(dA32, 1)
@@ -175,6 +179,25 @@ def streaming_rates(M, N, P, dev, iters=20):
     out["mxq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
     del aq_x, aq_q, aq_s, mq_s
     torch.cuda.empty_cache()
+    return out
+
+
+def pipeline_sweep(N, K, P, dev, steps=10, warmup=3):
+    """The step at the sweep's other sizes (M=8192, and M=20000 zero-padded to
+    20096 = 157 * 128): time per step and per phase, HIP events as above."""
+    import torch
+    from block_scaled_fp8_bsgemm_amd.pipeline import WoBStep
+    out = {}
+    for M_real in (8192, 20000):
+        M = -(-M_real // 128) * 128
+        qa, sa, qb, sb, parts, wq, ws = build_inputs(M, N, K, P, dev, M_real=M_real)
+        step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P)
+        ms, phase_ms, _ = time_steps(step, steps, warmup)
+        out[str(M_real)] = {"M_padded": M, "steps": steps, "us_per_step": ms * 1e3,
+                            "phases_us": {k: v * 1e3 for k, v in phase_ms.items()},
+                            "gemm_TFLOP/s": 2.0 * M * N * K / (phase_ms["gemm"] * 1e-3) / 1e12}
+        del step, qa, sa, qb, sb, parts, wq, ws
+        torch.cuda.empty_cache()
     return out
 
 
@@ -341,6 +364,8 @@ def main():
         rec["streaming"] = streaming_rates(M, N, P, dev)
         print("[bench] mxfp8 GEMM alone", file=sys.stderr, flush=True)
         rec["mxfp8_gemm"] = mx_gemm_rate(dev)
+        print("[bench] pipeline sweep M=8192, 20000", file=sys.stderr, flush=True)
+        rec["pipeline_sweep"] = pipeline_sweep(N, K, P, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu_baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(M, N, K, P)

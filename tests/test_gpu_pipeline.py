@@ -60,3 +60,50 @@ def test_pipeline_vs_oracle_chain(M, N, K, bands):
     assert np.array_equal(y[band_rows:], y_ref[band_rows:])
     rows_same = np.nonzero(same)[0]
     assert np.array_equal(y[rows_same], y_ref[rows_same])
+
+
+@pytest.mark.parametrize("M", [8192, 16384, 20000])
+def test_pipeline_full_size(M):
+    """The pipeline sweep at its real shapes (N=7168, K=2048, 8 bands; M=20000
+    zero-padded to 20096 = 157 * 128).  The GEMM is checked at sampled
+    elements (a quarter of them in band 0, the reduce's input); every later
+    stage is checked bit for bit against the oracle applied to the device's
+    own input to that stage: the reduce of the device's band 0 and the 7
+    stand-in bands, the row quantize of the device's reduced band, and the
+    dequantize of the wire buffer holding the device's codes."""
+    N, K, bands = synth.HIDDEN, synth.K_SHARD, synth.P_RANKS
+    Mp = -(-M // 128) * 128
+    band_rows = Mp // bands
+    say(f"pipeline full size M={M} (padded {Mp}) bands={bands}")
+    A, B = synth.operand_fp32(M, N, K, seed=0, heavy=True)
+    A = synth.pad_rows(A, Mp)
+    qa, sa = oracle.quant_blocks(A, 1, 128)
+    qb, sb = oracle.quant_blocks(B, 128, 128)
+    del A, B
+    parts = synth.partial_bands(band_rows, N, P=bands, seed0=100)[1:]
+    wq, ws = oracle.rowq(synth.wire_rows(Mp, N, seed=200))
+
+    step = WoBStep(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), [bf16_dev(p) for p in parts],
+                   to_dev(wq), to_dev(ws), bands)
+    step.step()
+    torch.cuda.synchronize()
+    c = bits16(step.C).reshape(Mp, N)
+
+    mi, ni = synth.sample_indices(Mp, N, 24576, seed=M)
+    m0, n0 = synth.sample_indices(band_rows, N, 8192, seed=M + 1)
+    mi, ni = np.concatenate([mi, m0]), np.concatenate([ni, n0])
+    _, e_ref = oracle.bsgemm_elems(qa, sa, qb, sb, mi, ni)
+    _, e_ref_m = oracle.bsgemm_elems(qa, sa, qb, sb, mi, ni, mfma=True)
+    gemm_compare(c[mi, ni], e_ref_m, e_ref, f"pipeline M={Mp} sampled")
+    assert np.all(c[M:] == 0)
+
+    red = bits16(step.reduced)
+    assert np.array_equal(red, oracle.band_reduce([c[:band_rows]] + parts))
+    q_dev = step.own_q.cpu().numpy()
+    s_dev = step.own_s.cpu().numpy()
+    q_ref, s_ref = oracle.rowq(red)
+    assert np.array_equal(q_dev, q_ref)
+    assert np.array_equal(s_dev.view(np.uint32), s_ref.view(np.uint32))
+    wq_ref, ws_ref = wq.copy(), ws.copy()
+    wq_ref[:band_rows], ws_ref[:band_rows] = q_ref, s_ref
+    assert np.array_equal(bits16(step.out), oracle.rowdq(wq_ref, ws_ref))
