@@ -635,14 +635,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     }
     __syncthreads();
     const int64_t n = n0 + (lane & 31) * 8;
+    // Row m0 + ml lies in band d0 + (r0 + ml) / band_rows at row (r0 + ml) %
+    // band_rows, with d0, r0 those of the tile's first row (rows < 2^31): one
+    // division per tile; with bands of at least 256 rows a tile row crosses at
+    // most one band boundary, so a compare replaces the per-row division.
+    const uint32_t br = (uint32_t)g.band_rows;
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane((uint32_t)m0 / br);
+    const uint32_t r0 = (uint32_t)m0 - d0 * br;
 #pragma unroll
     for (int r = 0; r < BM / 8 / 2; r++) {
         const int ml = wave * (BM / 8) + r * 2 + (lane >> 5);
         const u32x4 v = *(const u32x4 *)(out_row(ml) + (((lane & 31) * 16) ^ ((ml & 15) << 5)));
-        const int64_t m = m0 + ml;
-        if (m >= g.M || n >= g.N) continue;
-        const int64_t d = m / g.band_rows;
-        uint16_t *crow = g.C + d * g.band_stride + (m - d * g.band_rows) * g.N;
+        if (m0 + ml >= g.M || n >= g.N) continue;
+        uint32_t rr = r0 + (uint32_t)ml, d = d0;
+        if (br >= BM) {
+            const bool carry = rr >= br;
+            rr = carry ? rr - br : rr;
+            d = carry ? d + 1 : d;
+        } else {
+            d += rr / br;
+            rr = rr % br;
+        }
+        uint16_t *crow = g.C + (int64_t)d * g.band_stride + (int64_t)rr * g.N;
         *(u32x4 *)(crow + n) = v;
     }
 }
