@@ -36,10 +36,16 @@ HOST_LEAD_CYCLES = 4_000_000  # spin-kernel cycles (~2 ms) queued ahead of a tim
 
 
 def kernel_hash():
+    """Hash of the GEMM kernel's source with comments and whitespace removed, so
+    that the stored counter readings stay tied to the code, not its comments."""
+    import re
     h = hashlib.sha256()
     for f in ("gemm.hip", "codec.hpp"):
-        with open(os.path.join(ROOT, "block_scaled_fp8_bsgemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "block_scaled_fp8_bsgemm_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

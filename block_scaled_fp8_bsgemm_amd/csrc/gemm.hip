@@ -22,14 +22,20 @@
 //    sub-tiles, 128 fp32 accumulator registers per lane);
 //  - the MFMA takes the B fragment as its first operand, so each lane ends up
 //    holding 4 consecutive output columns of one output row: one combined
-//    scale per lane per sub-tile row, and 8-byte stores in the epilogue;
-//  - the combined scales a_scale * b_scale for the tile's 256 rows and its two
-//    128-column b_scale blocks are formed once per K block by the loader
-//    lanes and kept in LDS next to the operands;
+//    scale per lane per sub-tile row;
+//  - the K block's a_scale values of the tile's 256 rows and its b_scale
+//    values are DMA'd into LDS with the operands; each wave forms its rows'
+//    combined scales a_scale * b_scale in registers;
+//  - the bf16 tile is staged in LDS at the end so that every store writes
+//    whole 512-byte row segments of its destination band;
 //  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
 //    in groups of 8 M-tiles so that concurrently running tiles share A and B
 //    panels in that XCD's L2.
+//
+// A second blockscale kernel reads B in a prepacked form (the same bytes in the
+// MFMA's operand order, written once by bprepack_kernel) straight into
+// registers instead of staging it in LDS; its results are bit-identical.
 //
 // The same tile kernel is also built for the mxfp8 variant (sglang PR 43480,
 // "What" and "Not in this PR": e4m3 operands with one E8M0 scale byte per
@@ -108,7 +114,7 @@ struct Loader {
     int k8;      // 8 rows of a panel, in bytes
     int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
     int ldsq;    // byte offset of this wave's first 1 KiB LDS slot
-    int sdst;    // byte offset of this wave's 256-byte scale slot (waves 0..4)
+    int sdst;    // byte offset of this wave's 256-byte scale slot
 };
 
 // One DMA instruction of a stage load: pieces 0..7 are the A and B slots
