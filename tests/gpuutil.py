@@ -48,8 +48,9 @@ def poison_u8(t):
 
 
 def gemm_compare(got_bits, ref_mfma_bits, ref_exact_bits, what):
-    """bf16 GEMM output against O4m (relL2 <= 3e-5) and against the exact
-    block-sum definition O4 (no further than O4m itself is from O4)."""
+    """bf16 GEMM output against the oracle's MFMA model (O4m, or O11m for
+    mxfp8; relL2 <= 3e-5) and against its exact definition (O4 / O11: no
+    further than the model itself is from it)."""
     got = oracle.bf16_to_f64(got_bits)
     ref_m = oracle.bf16_to_f64(ref_mfma_bits)
     ref_e = oracle.bf16_to_f64(ref_exact_bits)
@@ -59,8 +60,8 @@ def gemm_compare(got_bits, ref_mfma_bits, ref_exact_bits, what):
     r_me = oracle.rel_l2(ref_m, ref_e)
     flips_m = int(np.count_nonzero(got_bits != ref_mfma_bits))
     flips_e = int(np.count_nonzero(got_bits != ref_exact_bits))
-    say(f"{what}: vs O4m relL2={r_m:.3e} differing={flips_m}/{got_bits.size}; "
-        f"vs O4 relL2={r_e:.3e} differing={flips_e} (O4m vs O4 {r_me:.3e})")
-    assert r_m <= GEMM_REL_L2, (what, "vs O4m", r_m)
-    assert r_e <= r_me + GEMM_REL_L2, (what, "vs O4", r_e, r_me)
+    say(f"{what}: vs MFMA model relL2={r_m:.3e} differing={flips_m}/{got_bits.size}; "
+        f"vs exact relL2={r_e:.3e} differing={flips_e} (model vs exact {r_me:.3e})")
+    assert r_m <= GEMM_REL_L2, (what, "vs MFMA model", r_m)
+    assert r_e <= r_me + GEMM_REL_L2, (what, "vs exact", r_e, r_me)
     return r_m, flips_m

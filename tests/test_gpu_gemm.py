@@ -142,3 +142,21 @@ def test_gemm_rejects_without_writing():
     assert e.value.status == bs.BS_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert np.all(bits16(C) == 0x7FC0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (3, 128, 8192), (200, 384, 8192)])
+def test_gemm_edge_shapes(M, N, K):
+    """One row; a single 128-column block; K = 8192 (64 K blocks, four times the
+    benchmark's depth, even and odd block counts are covered elsewhere)."""
+    say(f"bsgemm_fp8 edge M={M} N={N} K={K}")
+    qa, sa, qb, sb = operands(M, N, K, seed=5, heavy=True)
+    _, ref = oracle.bsgemm(qa, sa, qb, sb)
+    _, ref_m = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
+    C = run(qa, sa, qb, sb)
+    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"edge M={M} N={N} K={K}")
+    Bp = torch.empty(N * K, dtype=torch.uint8, device=device())
+    bs.bprepack_e4m3(to_dev(qb), Bp)
+    C2 = poison_bf16(torch.empty(M * N, dtype=torch.bfloat16, device=device()))
+    bs.bsgemm_fp8_pb(to_dev(qa), to_dev(sa), Bp, to_dev(sb), C2)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(C2), bits16(C))

@@ -168,3 +168,12 @@ def test_mxgemm_rejects_without_writing():
     assert e.value.status == bs.BS_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert np.all(bits16(C) == 0x7FC0)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 256), (3, 128, 8192), (200, 384, 8192)])
+def test_mxgemm_edge_shapes(M, N, K):
+    say(f"mxgemm_fp8 edge M={M} N={N} K={K}")
+    qa, ea, qb, eb = operands(M, N, K, seed=7, heavy=True)
+    _, ref = oracle.mxgemm(qa, ea, qb, eb)
+    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
+    gemm_compare(bits16(run(qa, ea, qb, eb)).reshape(M, N), ref_m, ref, f"mx edge M={M} N={N} K={K}")
