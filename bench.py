@@ -153,16 +153,23 @@ def streaming_rates(M, N, P, dev, iters=20):
              for i in range(nset)]
     rq_q = [torch.empty(band_rows, N, dtype=torch.uint8, device=dev) for _ in range(nset)]
     rq_s = [torch.empty(band_rows, dtype=torch.float32, device=dev) for _ in range(nset)]
-    del red_in
+    nset_red = len(red_in)
     t = timed(lambda i: bs.rowq_e4m3(rq_in[i], rq_q[i], rq_s[i]), nset)
     b = band_rows * N * 3 + band_rows * 4
     out["rowq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}
+    # the fused reduce + quantize of the same band (the pages' negative result):
+    # reads the P parts once, writes codes and scales; compare with band_reduce
+    # + rowq_e4m3 above
+    t = timed(lambda i: bs.band_rowq_e4m3(red_in[i], rq_q[i], rq_s[i]), nset_red)
+    b = P * band_rows * N * 2 + band_rows * N + band_rows * 4
+    out["band_rowq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS,
+                             "separate_us": out["band_reduce"]["us"] + out["rowq_e4m3"]["us"]}
     # rowdq: [16384,7168] u8 -> bf16: 352 MB per call; 4 sets
     nset = 4
     dq_q = [torch.randint(0, 0x7E, (M, N), dtype=torch.uint8, device=dev) for _ in range(nset)]
     dq_s = [torch.rand(M, device=dev) for _ in range(nset)]
     dq_y = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
-    del rq_in, rq_q, rq_s
+    del rq_in, rq_q, rq_s, red_in
     t = timed(lambda i: bs.rowdq_e4m3(dq_q[i], dq_s[i], dq_y[i]), nset)
     b = M * N * 3 + M * 4
     out["rowdq_e4m3"] = {"us": t * 1e6, "bytes": b, "GB/s": b / t / 1e9, "frac_hbm": b / t / 1e9 / PEAK_HBM_GBS}

@@ -15,6 +15,7 @@ library has not been built, importing the functions raises immediately.
   bprepack_e4m3(B, Bp=None)
   bsgemm_fp8_pb(A, a_scale, Bp, b_scale, C=None, bands=1, band_stride=0)
   mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0)
+  band_rowq_e4m3(parts, q=None, scale=None)
   mxq_e4m3(x, q=None, scale=None)
 
 Tensors: e4m3 codes are uint8 (or torch.float8_e4m3fn, reinterpreted), bf16
@@ -31,7 +32,8 @@ BS_OK, BS_ERR_INVALID, BS_ERR_UNSUPPORTED, BS_ERR_LAUNCH = 0, 1, 2, 3
 
 # every extern "C" symbol of include/bsgemm.h
 EXPORTS = ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
-           "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb", "bs_status_str")
+           "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb", "band_rowq_e4m3",
+           "bs_status_str")
 
 _lib = None
 
@@ -61,8 +63,9 @@ def load():
     L.mxq_e4m3.argtypes = [vp, vp, vp, i64, i64, vp]
     L.bprepack_e4m3.argtypes = [vp, vp, i64, i64, vp]
     L.bsgemm_fp8_pb.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i64, vp]
+    L.band_rowq_e4m3.argtypes = [ctypes.POINTER(vp), i32, vp, vp, i64, i64, vp]
     for f in ("bsgemm_fp8", "band_reduce", "rowq_e4m3", "rowdq_e4m3", "blockq_e4m3", "actq_e4m3",
-              "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb"):
+              "mxgemm_fp8", "mxq_e4m3", "bprepack_e4m3", "bsgemm_fp8_pb", "band_rowq_e4m3"):
         getattr(L, f).restype = ctypes.c_int
     L.bs_status_str.argtypes = [ctypes.c_int]
     L.bs_status_str.restype = ctypes.c_char_p
@@ -264,3 +267,22 @@ def bsgemm_fp8_pb(A, a_scale, Bp, b_scale, C=None, bands=1, band_stride=0, strea
                               _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
     _check(st, "bsgemm_fp8_pb")
     return C
+
+
+def band_rowq_e4m3(parts, q=None, scale=None, stream=None):
+    """(q uint8 [rows,N], scale fp32 [rows]) = rowq_e4m3(band_reduce(parts)) in one kernel."""
+    torch = _torch()
+    parts = list(parts)
+    rows, N = parts[0].shape
+    for p in parts:
+        if tuple(p.shape) != (rows, N):
+            raise ValueError("all parts must have the same shape")
+    if q is None:
+        q = torch.empty((rows, N), dtype=torch.uint8, device=parts[0].device)
+    if scale is None:
+        scale = torch.empty((rows,), dtype=torch.float32, device=parts[0].device)
+    ptrs = (ctypes.c_void_p * len(parts))(*[_ptr(p, _b16(), "part") for p in parts])
+    st = load().band_rowq_e4m3(ptrs, len(parts), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
+                               rows, N, _stream(stream))
+    _check(st, "band_rowq_e4m3")
+    return q, scale

@@ -147,6 +147,26 @@ bs_status band_reduce(const uint16_t *const *parts, int32_t P, uint16_t *out, in
     return bs_launch_band_reduce(parts, P, out, rows, N, as_stream(stream)) == 0 ? BS_OK : BS_ERR_LAUNCH;
 }
 
+bs_status band_rowq_e4m3(const uint16_t *const *parts, int32_t P, uint8_t *q, float *scale,
+                         int64_t rows, int64_t N, void *stream) {
+    if (!parts || !q || !scale || P < 1 || P > 16 || rows < 0 || N <= 0) return BS_ERR_INVALID;
+    for (int p = 0; p < P; p++)
+        if (!parts[p]) return BS_ERR_INVALID;
+    if (N % 8 || N > 8192 || rows >= kMaxDim) return BS_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(scale, 4)) return BS_ERR_UNSUPPORTED;
+    for (int p = 0; p < P; p++)
+        if (!aligned(parts[p], 16)) return BS_ERR_UNSUPPORTED;
+    const Range rq = range_of(q, rows * N), rs = range_of(scale, rows * 4);
+    if (overlap(rq, rs)) return BS_ERR_INVALID;
+    for (int p = 0; p < P; p++) {
+        const Range rp = range_of(parts[p], rows * N * 2);
+        if (overlap(rq, rp) || overlap(rs, rp)) return BS_ERR_INVALID;
+    }
+    if (rows == 0) return BS_OK;
+    return bs_launch_band_rowq(parts, P, q, scale, rows, N, as_stream(stream)) == 0 ? BS_OK
+                                                                                     : BS_ERR_LAUNCH;
+}
+
 bs_status rowq_e4m3(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t N,
                     void *stream) {
     if (!x || !q || !scale || rows < 0 || N <= 0) return BS_ERR_INVALID;

@@ -26,6 +26,8 @@ int bs_launch_rowdq(const uint8_t *q, const float *scale, uint16_t *y, int64_t r
 
 int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
                      int block_rows, hipStream_t stream);
+int bs_launch_band_rowq(const uint16_t *const *parts, int P, uint8_t *q, float *scale, int64_t rows,
+                        int64_t N, hipStream_t stream);
 int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
                    hipStream_t stream);
 int bs_launch_mxq(const uint16_t *x, uint8_t *q, uint8_t *e, int64_t rows, int64_t cols,

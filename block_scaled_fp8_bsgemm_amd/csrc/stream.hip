@@ -154,6 +154,68 @@ rowq_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restric
     }
 }
 
+// Fused reduce + row quantize (the pages' "Negative results" experiment): one
+// wavefront per row of the reduced band.  Each lane sums its CPL packs over
+// the P parts in part order from +0 in fp32 (one part's packs in flight at a
+// time), rounds the sums to bf16 as band_reduce does, and then quantizes
+// those bf16 values exactly as rowq_kernel does: the result equals
+// rowq(band_reduce(parts)) bit for bit, without the bf16 band in memory.
+template <int CPL>
+__global__ void __launch_bounds__(256)
+band_rowq_kernel(PartPtrs parts, int P, u32x2 *__restrict__ q, float *__restrict__ scale,
+                 int64_t rows, int nch) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    float acc[CPL][8];
+#pragma unroll
+    for (int i = 0; i < CPL; i++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[i][e] = 0.0f;
+    for (int p = 0; p < P; p++) {
+        const u32x4 *xr = parts.p[p] + row * nch;
+        u32x4 w[CPL];
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int c = lane + 64 * i;
+            if (c < nch) w[i] = __builtin_nontemporal_load(xr + c);
+        }
+#pragma unroll
+        for (int i = 0; i < CPL; i++) {
+            const int c = lane + 64 * i;
+            if (c < nch) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    acc[i][2 * e] += bf16_lo(w[i][e]);
+                    acc[i][2 * e + 1] += bf16_hi(w[i][e]);
+                }
+            }
+        }
+    }
+    u32x4 v[CPL];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int c = lane + 64 * i;
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[i][e] = pack_bf16x2(acc[i][2 * e], acc[i][2 * e + 1]);
+        if (c < nch) amax = fmaxf(amax, pack_absmax(v[i]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / 448.0f;
+    if (lane == 0) scale[row] = s;
+    u32x2 *qr = q + row * nch;
+    const double R = s != 0.0f ? 1.0 / (double)s : 0.0;
+#pragma unroll
+    for (int i = 0; i < CPL; i++) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+            const u32x2 o = s != 0.0f ? quant_pack(v[i], R) : (u32x2){0u, 0u};
+            __builtin_nontemporal_store(o, qr + c);
+        }
+    }
+}
+
 // Rows longer than the register-resident variant: amax pass, then a second
 // pass that re-reads the row (from L2) and encodes it.
 __global__ void __launch_bounds__(256)
@@ -491,4 +553,19 @@ int bs_launch_mxq(const uint16_t *x, uint8_t *q, uint8_t *e, int64_t rows, int64
     if (blocks < 1) blocks = 1;
     return bs_enqueue(mxq_1x32_kernel, dim3((unsigned)blocks), dim3(256), stream, (const u32x4 *)x,
                       (u32x2 *)q, e, npack);
+}
+
+int bs_launch_band_rowq(const uint16_t *const *parts, int P, uint8_t *q, float *scale, int64_t rows,
+                        int64_t N, hipStream_t stream) {
+    PartPtrs pp;
+    for (int p = 0; p < 16; p++) pp.p[p] = (const u32x4 *)parts[p < P ? p : 0];
+    const int nch = (int)(N / 8);
+    const int64_t wg = (rows + 3) / 4;
+    if (wg > 0x7FFFFFFF || nch > 1024) return -1;
+    const dim3 grid((unsigned)wg), block(256);
+    u32x2 *qv = (u32x2 *)q;
+    if (nch <= 256) return bs_enqueue(band_rowq_kernel<4>, grid, block, stream, pp, P, qv, scale, rows, nch);
+    if (nch <= 512) return bs_enqueue(band_rowq_kernel<8>, grid, block, stream, pp, P, qv, scale, rows, nch);
+    if (nch <= 896) return bs_enqueue(band_rowq_kernel<14>, grid, block, stream, pp, P, qv, scale, rows, nch);
+    return bs_enqueue(band_rowq_kernel<16>, grid, block, stream, pp, P, qv, scale, rows, nch);
 }

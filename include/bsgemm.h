@@ -6,6 +6,9 @@
  *                destination-major row bands
  *   band_reduce  fp32 sum of P bf16 partial bands into one bf16 band
  *   rowq_e4m3    per-row e4m3 quantize with one fp32 scale per row
+ *   band_rowq_e4m3  band_reduce and rowq_e4m3 fused into one pass (the fused
+ *                variant the pages measured and found slower; kept to
+ *                reproduce that measurement)
  *   rowdq_e4m3   per-row e4m3 dequantize back to bf16
  *   blockq_e4m3  fp32 operand -> e4m3 codes + fp32 block scales (the
  *                activation/weight quantizer that produces bsgemm_fp8's input)
@@ -285,6 +288,24 @@ bs_status mxgemm_fp8(const uint8_t *A, const uint8_t *a_scale,
  */
 bs_status mxq_e4m3(const uint16_t *x, uint8_t *q, uint8_t *scale,
                    int64_t rows, int64_t cols, void *stream);
+
+/*
+ * band_reduce followed by rowq_e4m3, fused into one kernel that never writes
+ * the bf16 band: q, scale = rowq_e4m3(band_reduce(parts)), bit for bit (the
+ * fp32 part-order sum is rounded to bf16 before the row quantizer sees it).
+ * [MORI] "Negative results" reports that fusing the reduce with the quantize
+ * was slower than the two separate kernels, because a row's amax forces one
+ * wavefront per row; this entry point reproduces that comparison.
+ *
+ *   parts  host array of P device pointers, each bf16 [rows, N] (1 <= P <= 16)
+ *   q      e4m3 [rows, N];  scale  fp32 [rows]
+ *
+ * Requirements: rows >= 0; N > 0, N % 8 == 0, N <= 8192; parts and q 16-byte
+ * aligned, scale 4-byte aligned; no output overlaps a part or the other
+ * output.
+ */
+bs_status band_rowq_e4m3(const uint16_t *const *parts, int32_t P, uint8_t *q,
+                         float *scale, int64_t rows, int64_t N, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *bs_status_str(bs_status status);

@@ -179,3 +179,19 @@ def test_bprepack_rejections(L):
     assert f(P, P + 0x100008, 512, 256, None) == UNS
     assert f(P, P, 512, 256, None) == INV                                 # in place
     assert f(P, P + 512 * 256 - 16, 512, 256, None) == INV               # overlapping
+
+
+def test_band_rowq_rejections(L):
+    parts = (ctypes.c_void_p * 4)(P, P + 0x100000, P + 0x200000, P + 0x300000)
+    f = L.band_rowq_e4m3
+    Q, S = P + 0x1000000, P + 0x2000000
+    assert f(None, 4, Q, S, 64, 1024, None) == INV
+    assert f(parts, 0, Q, S, 64, 1024, None) == INV and f(parts, 17, Q, S, 64, 1024, None) == INV
+    assert f(parts, 4, 0, S, 64, 1024, None) == INV and f(parts, 4, Q, 0, 64, 1024, None) == INV
+    assert f(parts, 4, Q, S, -1, 1024, None) == INV and f(parts, 4, Q, S, 64, 0, None) == INV
+    assert f(parts, 4, Q, S, 64, 1020, None) == UNS                 # N % 8
+    assert f(parts, 4, Q, S, 64, 8200, None) == UNS                 # N > 8192
+    assert f(parts, 4, Q + 8, S, 64, 1024, None) == UNS and f(parts, 4, Q, S + 2, 64, 1024, None) == UNS
+    assert f(parts, 4, P + 4096, S, 64, 1024, None) == INV          # q over part 0
+    assert f(parts, 4, Q, Q + 1024, 64, 1024, None) == INV          # scale over q
+    assert f(parts, 4, Q, S, 0, 1024, None) == OK

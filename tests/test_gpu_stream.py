@@ -182,3 +182,26 @@ def test_actq_matches_blockq():
     q2, s2 = bs.blockq_e4m3(to_dev(x32), 1)
     torch.cuda.synchronize()
     assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+@pytest.mark.parametrize("rows,N,P", [(2048, 7168, 8), (37, 104, 3), (5, 8, 1), (130, 8192, 16), (64, 2048, 8)])
+def test_band_rowq_bitexact(rows, N, P):
+    """The fused reduce + row quantize equals the oracle's row quantize of its
+    band reduce, and the device's two separate kernels, bit for bit."""
+    say(f"band_rowq_e4m3 rows={rows} N={N} P={P}")
+    parts = synth.partial_bands(rows, N, P=P, seed0=300)
+    parts[0][min(2, rows - 1)] = 0                    # a zero row in one part only
+    if P > 1:
+        for p in parts:
+            p[rows - 1] = 0                           # a row that sums to +0
+    red_ref = oracle.band_reduce(parts)
+    q_ref, s_ref = oracle.rowq(red_ref)
+    dparts = [bf16_dev(p) for p in parts]
+    q = poison_u8(torch.empty((rows, N), dtype=torch.uint8, device=device()))
+    s = torch.full((rows,), float("nan"), dtype=torch.float32, device=device())
+    bs.band_rowq_e4m3(dparts, q, s)
+    q2, s2 = bs.rowq_e4m3(bs.band_reduce(dparts))
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert torch.equal(q, q2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
