@@ -12,7 +12,8 @@ average time and rate inside the timed steps; `roofline` is the GEMM's
 HBM-bound kernels measured alone on rotating buffers (>1 GiB, so the 256 MB
 Infinity Cache cannot serve repeats); `mxfp8_gemm` is the mxfp8 variant of the
 GEMM alone at M=16384, N=5120, K=2048; `pipeline_sweep` gives the step at
-M=8192 and M=20000 (padded to 20096); `cpu_baseline` is the CPU oracle timed
+M=8192 and M=20000 (padded to 20096); `gemm_k_sweep` fits the GEMM's time at
+K=512..4096 as fixed + per-K-block cost; `cpu_baseline` is the CPU oracle timed
 on a bounded row sample of the same workload and projected to a full step.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
@@ -214,6 +215,43 @@ def pipeline_sweep(N, K, P, dev, steps=10, warmup=3):
     return out
 
 
+def gemm_k_sweep(dev, iters=10):
+    """The blockscale GEMM at M=16384, N=7168, 8 bands and K = 512 .. 4096,
+    fitted as t = fixed + per_kblock * K/128 (the decomposition the MORI
+    benchmark page uses to compare GEMMs, "Negative results": a CK-shaped
+    kernel).  Operands: device N(0,1) / 0.02 N(0,1) draws, block-quantized."""
+    import numpy as np
+    import torch
+    import block_scaled_fp8_bsgemm_amd as bs
+    M, N = 16384, 7168
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    Ks, ts = [512, 1024, 2048, 4096], []
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    for K in Ks:
+        qa, sa = bs.blockq_e4m3(torch.randn(M, K, device=dev, generator=g), 1)
+        qb, sb = bs.blockq_e4m3(0.02 * torch.randn(N, K, device=dev, generator=g), 128)
+        for _ in range(3):
+            bs.bsgemm_fp8(qa, sa, qb, sb, C, bands=8)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(HOST_LEAD_CYCLES)
+        e0.record()
+        for _ in range(iters):
+            bs.bsgemm_fp8(qa, sa, qb, sb, C, bands=8)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / iters * 1e3)
+        del qa, sa, qb, sb
+    kb = np.array(Ks, dtype=np.float64) / 128
+    per, fixed = np.polyfit(kb, np.array(ts), 1)
+    torch.cuda.empty_cache()
+    return {"M": M, "N": N, "K": Ks, "us": ts, "fixed_us": float(fixed), "per_kblock_us": float(per),
+            "pages_mori_gemm": {"fixed_us": 51.6, "per_kblock_us": 20.9},
+            "pages_ck_gemm": {"fixed_us": 66.0, "per_kblock_us": 14.5}}
+
+
 def mx_gemm_rate(dev, iters=20):
     """The mxfp8 variant of the GEMM alone at M=16384, N=5120, K=2048 (one
     band), seeded random codes with E8M0 scales around 2^0."""
@@ -377,6 +415,8 @@ def main():
         rec["streaming"] = streaming_rates(M, N, P, dev)
         print("[bench] mxfp8 GEMM alone", file=sys.stderr, flush=True)
         rec["mxfp8_gemm"] = mx_gemm_rate(dev)
+        print("[bench] GEMM K sweep", file=sys.stderr, flush=True)
+        rec["gemm_k_sweep"] = gemm_k_sweep(dev)
         print("[bench] pipeline sweep M=8192, 20000", file=sys.stderr, flush=True)
         rec["pipeline_sweep"] = pipeline_sweep(N, K, P, dev)
     if not args.no_cpu_baseline:
