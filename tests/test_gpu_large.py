@@ -1,0 +1,67 @@
+"""Maximum-size cases on the device (an MI355X holds 288 GB): the dequantizer
+past 2^31 packs, where it switches to 64-bit indices, and the GEMM with a
+14 GiB output written as 8 bands, where row offsets pass 2^32 bytes.  Inputs
+are drawn on the device; sampled outputs are checked against the oracle on
+the sampled rows only, so nothing large crosses to the host."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_bsgemm_amd as bs
+import oracle
+import synth
+from gpuutil import bits16, device, gemm_compare, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_rowdq_64bit_index():
+    rows, N = 1 << 21, 8192                     # 2^34 codes = 2^31 packs of 8
+    dev = device()
+    say(f"rowdq_e4m3 rows={rows} N={N} (64-bit index path)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    q = torch.randint(0, 0x7F, (rows, N), dtype=torch.uint8, device=dev, generator=g)   # no NaN codes
+    q |= torch.randint(0, 2, (rows, N), dtype=torch.uint8, device=dev, generator=g) << 7
+    s = torch.rand(rows, device=dev, generator=g) * 4.0
+    y = bs.rowdq_e4m3(q, s)
+    torch.cuda.synchronize()
+    mi, ni = synth.sample_indices(rows, N, 65536, seed=3)
+    mi = np.concatenate([mi, np.full(64, rows - 1), np.arange(rows - 64, rows)])
+    ni = np.concatenate([ni, np.arange(N - 64, N), np.full(64, N - 1)])
+    tm, tn = torch.from_numpy(mi).to(dev), torch.from_numpy(ni).to(dev)
+    qs = q[tm, tn].cpu().numpy()
+    ss = s[tm].cpu().numpy()
+    ys = y[tm, tn].view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.rowdq(qs[:, None], ss)[:, 0]
+    del q, y
+    torch.cuda.empty_cache()
+    assert np.array_equal(ys, ref)
+
+
+def test_gemm_output_past_4gib():
+    M, N, K, bands = 1 << 20, 7168, 256, 8     # C: 14 GiB in 8 bands of 1.75 GiB
+    dev = device()
+    say(f"bsgemm_fp8 M={M} N={N} K={K} bands={bands} (C past 2^32 bytes)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(22)
+    qa, sa = bs.blockq_e4m3(torch.randn(M, K, device=dev, generator=g), 1)
+    qb, sb = bs.blockq_e4m3(0.02 * torch.randn(N, K, device=dev, generator=g), 128)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    C.view(torch.int16).fill_(0x7FC0)
+    bs.bsgemm_fp8(qa, sa, qb, sb, C, bands=bands)
+    torch.cuda.synchronize()
+    mi, ni = synth.sample_indices(M, N, 16384, seed=4)
+    edge = np.array([M // bands * d + o for d in range(bands) for o in (0, M // bands - 1)])
+    mi = np.concatenate([mi, np.repeat(edge, 16), np.full(16, M - 1)])
+    ni = np.concatenate([ni, np.tile(np.linspace(0, N - 1, 16).astype(np.int64), edge.size + 1)])
+    tm = torch.from_numpy(mi).to(dev)
+    got = C.view(M, N)[tm, torch.from_numpy(ni).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+    qa_s, sa_s = qa[tm].cpu().numpy(), sa[tm].cpu().numpy()
+    qb_h, sb_h = qb.cpu().numpy(), sb.cpu().numpy()
+    del C, qa, sa
+    torch.cuda.empty_cache()
+    rows = np.arange(mi.size)
+    _, ref = oracle.bsgemm_elems(qa_s, sa_s, qb_h, sb_h, rows, ni)
+    _, ref_m = oracle.bsgemm_elems(qa_s, sa_s, qb_h, sb_h, rows, ni, mfma=True)
+    gemm_compare(got, ref_m, ref, f"M={M} sampled")
