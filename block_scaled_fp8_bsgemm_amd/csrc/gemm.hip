@@ -14,8 +14,9 @@
 //
 // Tiling (one workgroup = 8 waves = 512 lanes, one 256x256 output tile):
 //  - per K block the A tile [256 x 128 B] and B tile [256 x 128 B] are staged
-//    in LDS, double buffered (2 x 64 KiB); 16-byte chunks are XOR-swizzled by
-//    row so the MFMA operand reads hit distinct banks;
+//    in LDS, double buffered (2 x 64 KiB); rows are placed in even / odd
+//    128-byte slots and 16-byte chunks XOR-swizzled (swz) so that every MFMA
+//    operand read is served without bank conflicts;
 //  - global loads use buffer descriptors sized to the matrix, so rows past M
 //    (a ragged last tile) read as zero without any branch;
 //  - waves form a 2 (M) x 4 (N) grid of 128 x 64 wave tiles (8 x 4 MFMA
@@ -96,9 +97,16 @@ template <int ST> __device__ __forceinline__ uint8_t *stB() { return ST ? sB1 : 
 template <int ST> __device__ __forceinline__ float *stS() { return ST ? sS1 : sS0; }
 
 
-// byte offset of 16-byte chunk `c` (0..7) of tile row `r` inside a staged
-// [rows x 128 B] operand tile: chunks are XOR-swizzled by the row's low bits
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk `c` (0..7) of tile row `r` inside a staged
+// [rows x 128 B] operand tile.  An MFMA fragment read (ds_read_b128) has each
+// 16-lane quarter read one chunk of 16 consecutive rows, and the LDS serves
+// such a quarter in one pass only when lanes 0-7 fall in the lower 128 bytes
+// of the bank array (banks 0-31) and lanes 8-15 in the upper 128 bytes, each
+// half without conflicts.  So within every 16-row group, rows 0-7 go to the
+// even 128-byte slots and rows 8-15 to the odd ones, and chunks are
+// XOR-swizzled by the row's low three bits.
+__device__ __forceinline__ int lds_slot(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return lds_slot(r) * 128 + ((c ^ (r & 7)) << 4); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     int32_t n = bytes > 0x7FFFFFFFll ? 0x7FFFFFFF : (bytes > 0 ? (int32_t)bytes : 0);
@@ -110,8 +118,9 @@ struct Loader {
     __amdgpu_buffer_rsrc_t rZ;           // zero-size: every load through it reads nothing
     int poff;    // prepacked B: this lane's byte offset in its wave's first fragment
     int pstep;   // prepacked B: bytes from one 16-row group to the next (K/128 * 2 KiB)
-    int voff;    // this lane's byte offset of its chunk in the A / B row panels
-    int k8;      // 8 rows of a panel, in bytes
+    int voff;    // this lane's byte offset of its chunk in the A / B row panels (even slots i)
+    int voff1;   // the same for odd slots i (the lane's chunk with bit 2 flipped)
+    int k4;      // 4 rows of a panel, in bytes
     int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
     int ldsq;    // byte offset of this wave's first 1 KiB LDS slot
     int sdst;    // byte offset of this wave's 256-byte scale slot
@@ -127,12 +136,14 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
     if (PIECE < 8) {
         const int i = PIECE >> 1;
         const int q = L.ldsq + i * 1024;
+        // slot i's rows are those of slot 0 plus 0, 4, 16, 20 (see load_stage)
+        const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4;
         if (PIECE & 1)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rB : L.rZ, (lds_void *)(stB<ST>() + q),
-                                                     16, L.voff + i * L.k8, koff, 0, 0);
+                                                     16, vo, koff, 0, 0);
         else
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rA : L.rZ, (lds_void *)(stA<ST>() + q),
-                                                     16, L.voff + i * L.k8, koff, 0, 0);
+                                                     16, vo, koff, 0, 0);
     } else {
         // blockscale: waves 0..3 fetch a_scale of rows 64w..64w+63, waves
         // 4..7 b_scale of the column blocks from the tile's first one on;
@@ -146,9 +157,13 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
 }
 
 // DMA the K block kb of the A and B panels and of the scales into stage ST.
-// One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order;
-// lane l of slot q lands on row 8q + l/8 at physical chunk l%8, so it fetches
-// logical chunk (l%8) ^ (l/8) of that row, which realises the swizzle.
+// One buffer_load ... lds writes 64 lanes x 16 B = 1 KiB of LDS in lane order:
+// eight 128-byte row slots, lane l on slot l/8 at physical chunk l%8.  Wave w's
+// slot i (0..3) covers LDS slots 32w + 8i .. 32w + 8i + 7, which hold tile rows
+// 32w + {0, 4, 16, 20}[i] + (l/16) + 8 * ((l/8) % 2) (lds_slot inverted), so
+// every instruction still fetches eight whole 128-byte row segments; the lane
+// fetches logical chunk (l%8) ^ (row & 7) of its row, which realises the
+// swizzle.
 template <int ST>
 __device__ __forceinline__ void load_stage(const Loader &L, int kb, bool valid = true) {
     dma_piece<ST, 0>(L, kb, valid); dma_piece<ST, 1>(L, kb, valid);
@@ -516,10 +531,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     L.rZ = make_rsrc(g.A, 0);
     L.ldsq = wave * 4096;
     {
-        const int row = wave * 32 + (lane >> 3);   // + 8 per slot i
-        const int chunk = (lane & 7) ^ (lane >> 3);
+        // slot 0's row and chunk of this lane (see load_stage); the odd slots'
+        // rows are 4 further on, so their row & 7 has bit 2 set
+        const int row = wave * 32 + (lane >> 4) + 8 * ((lane >> 3) & 1);
+        const int chunk = (lane & 7) ^ (lane >> 4);
         L.voff = row * (int)K + chunk * 16;
-        L.k8 = 8 * (int)K;
+        L.voff1 = L.voff ^ 64;
+        L.k4 = 4 * (int)K;
         L.soff = MX ? ((wave & 3) * 64 + lane) * KQ : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
         L.sdst = wave * 256;
     }
