@@ -2,8 +2,10 @@
 
 One step = the whole hot path over one batch: block-scale fp8 GEMM
 (M=16384, N=7168, K=2048) written as 8 destination-major bands, the fp32
-reduce of the own band with 7 stand-in partial bands, per-row e4m3 quantize
-of the reduced band, and dequantize of the [16384, 7168] wire buffer.
+reduce of the own band with 7 stand-in partial bands fused with the per-row
+e4m3 quantize of the reduced band (one kernel, the same codes and scales as
+the two separate calls), and dequantize of the [16384, 7168] wire buffer.
+`unfused_step` times the same step with reduce and quantize as two calls.
 
 Prints ONE JSON line.  `value` is whole-step throughput expressed in GEMM
 TFLOP/s (2*M*N*K per step / step time); `phases` gives each kernel's own
@@ -236,7 +238,7 @@ def pipeline_sweep(N, K, P, dev, steps=10, warmup=3):
     for M_real in (8192, 20000):
         M = -(-M_real // 128) * 128
         qa, sa, qb, sb, parts, wq, ws = build_inputs(M, N, K, P, dev, M_real=M_real)
-        step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P)
+        step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P, fused=True)
         ramp_clock(step, 100)
         ms, gemm_ms, phase_ms, _ = time_steps(step, steps, warmup)
         out[str(M_real)] = {"M_padded": M, "steps": steps, "us_per_step": ms * 1e3,
@@ -390,23 +392,29 @@ def main():
     M, N, K, P = 16384, 7168, 2048, 8
     print(f"[bench] building inputs M={M} N={N} K={K} P={P}", file=sys.stderr, flush=True)
     qa, sa, qb, sb, parts, wq, ws = build_inputs(M, N, K, P, dev)
-    step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P)
+    step = WoBStep(qa, sa, qb, sb, parts, wq, ws, P, fused=True)
     ramp_clock(step)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
     ms, gemm_ms, phase_ms, wall = time_steps(step, args.steps, args.warmup)
+    print("[bench] the same step with reduce and quantize as two calls", file=sys.stderr, flush=True)
+    step_u = WoBStep(qa, sa, qb, sb, parts, wq, ws, P)
+    ramp_clock(step_u, 100)
+    ms_u, _, phase_u, _ = time_steps(step_u, args.steps, args.warmup)
+    del step_u
 
     flops = 2.0 * M * N * K
     band_rows = M // P
     gemm_s = gemm_ms * 1e-3
     gemm_tflops = flops / gemm_s / 1e12
     bytes_of = {
+        "reduce_quantize": P * band_rows * N * 2 + band_rows * N + band_rows * 4,
         "reduce": P * band_rows * N * 2 + band_rows * N * 2,
         "quantize": band_rows * N * 2 + band_rows * N + band_rows * 4,
         "dequantize": M * N + M * 4 + M * N * 2,
     }
     phases = {"gemm": {"us": phase_ms["gemm"] * 1e3, "TFLOP/s": flops / (phase_ms["gemm"] * 1e-3) / 1e12,
                        "timed_region_us": gemm_ms * 1e3}}
-    for ph in ("reduce", "quantize", "dequantize"):
+    for ph in step.PHASES[1:]:
         t = phase_ms[ph] * 1e-3
         phases[ph] = {"us": t * 1e6, "bytes": bytes_of[ph], "GB/s": bytes_of[ph] / t / 1e9}
     traffic = load_traffic()
@@ -424,13 +432,15 @@ def main():
         "vs_baseline": value / (flops / (PAGES_STEP_US * 1e-6) / 1e12),
         "dtype": "e4m3",
         "data": "synthetic",
-        "config": {"workload": "wo_b per-GPU step (blockscale fp8 GEMM + 8-band epilogue, band reduce P=8, "
-                               "row e4m3 quantize, dequantize)",
+        "config": {"workload": "wo_b per-GPU step (blockscale fp8 GEMM + 8-band epilogue, band reduce P=8 "
+                               "fused with row e4m3 quantize, dequantize)",
                    "M": M, "N": N, "K": K, "P": P, "bands": P},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,
                      "kernel": "bsgemm_tile_kernel", "algorithmic_flop_per_launch": flops},
         "phases": phases,
+        "unfused_step": {"ms_per_step": ms_u, "value": flops / (ms_u * 1e-3) / 1e12,
+                         "phases_us": {k: v * 1e3 for k, v in phase_u.items()}},
         "wall_s_timed": wall,
     }
     if args.calib_copy:

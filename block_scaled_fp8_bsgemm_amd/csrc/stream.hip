@@ -155,60 +155,71 @@ rowq_kernel(const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restric
 }
 
 // Fused reduce + row quantize (the pages' "Negative results" experiment): one
-// wavefront per row of the reduced band.  Each lane sums its CPL packs over
-// the P parts in part order from +0 in fp32 (one part's packs in flight at a
-// time), rounds the sums to bf16 as band_reduce does, and then quantizes
-// those bf16 values exactly as rowq_kernel does: the result equals
-// rowq(band_reduce(parts)) bit for bit, without the bf16 band in memory.
-template <int CPL>
+// 256-lane workgroup per row of the reduced band, lane t owning packs t,
+// t + 256, t + 512, t + 768 of the row (N <= 8192).  The parts are read G at
+// a time with every load of the group in flight before the adds (non-temporal:
+// each part is read once), and each lane sums its packs over the P parts in
+// part order from +0 in fp32; the sums are rounded to bf16 as band_reduce
+// does, the row amax goes through one LDS exchange between the four
+// wavefronts, and the bf16 values are quantized exactly as rowq_kernel does.
+// The result equals rowq(band_reduce(parts)) bit for bit, without the bf16
+// band in memory.
+constexpr int BRQ_CPT = 4;   // packs per lane: rows of up to 4 * 256 packs
+template <int G>
 __global__ void __launch_bounds__(256)
-band_rowq_kernel(PartPtrs parts, int P, u32x2 *__restrict__ q, float *__restrict__ scale,
-                 int64_t rows, int nch) {
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;
-    float acc[CPL][8];
+band_rowq_kernel(PartPtrs parts, int P, u32x2 *__restrict__ q, float *__restrict__ scale, int nch) {
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t base = row * nch;
+    float acc[BRQ_CPT][8];
 #pragma unroll
-    for (int i = 0; i < CPL; i++)
+    for (int i = 0; i < BRQ_CPT; i++)
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[i][e] = 0.0f;
-    for (int p = 0; p < P; p++) {
-        const u32x4 *xr = parts.p[p] + row * nch;
-        u32x4 w[CPL];
+    for (int p0 = 0; p0 < P; p0 += G) {
+        u32x4 w[G][BRQ_CPT];
 #pragma unroll
-        for (int i = 0; i < CPL; i++) {
-            const int c = lane + 64 * i;
-            if (c < nch) w[i] = __builtin_nontemporal_load(xr + c);
-        }
+        for (int g = 0; g < G; g++)
 #pragma unroll
-        for (int i = 0; i < CPL; i++) {
-            const int c = lane + 64 * i;
-            if (c < nch) {
+            for (int i = 0; i < BRQ_CPT; i++) {
+                const int c = tid + 256 * i;
+                if (p0 + g < P && c < nch) w[g][i] = __builtin_nontemporal_load(parts.p[p0 + g] + base + c);
+            }
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    acc[i][2 * e] += bf16_lo(w[i][e]);
-                    acc[i][2 * e + 1] += bf16_hi(w[i][e]);
+        for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int i = 0; i < BRQ_CPT; i++) {
+                const int c = tid + 256 * i;
+                if (p0 + g < P && c < nch) {
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        acc[i][2 * e] += bf16_lo(w[g][i][e]);
+                        acc[i][2 * e + 1] += bf16_hi(w[g][i][e]);
+                    }
                 }
             }
-        }
     }
-    u32x4 v[CPL];
+    u32x4 v[BRQ_CPT];
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; i++) {
-        const int c = lane + 64 * i;
+    for (int i = 0; i < BRQ_CPT; i++) {
+        const int c = tid + 256 * i;
 #pragma unroll
         for (int e = 0; e < 4; e++) v[i][e] = pack_bf16x2(acc[i][2 * e], acc[i][2 * e + 1]);
         if (c < nch) amax = fmaxf(amax, pack_absmax(v[i]));
     }
     amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = amax / 448.0f;
-    if (lane == 0) scale[row] = s;
-    u32x2 *qr = q + row * nch;
+    if (tid == 0) scale[row] = s;
+    u32x2 *qr = q + base;
     const double R = s != 0.0f ? 1.0 / (double)s : 0.0;
 #pragma unroll
-    for (int i = 0; i < CPL; i++) {
-        const int c = lane + 64 * i;
+    for (int i = 0; i < BRQ_CPT; i++) {
+        const int c = tid + 256 * i;
         if (c < nch) {
             const u32x2 o = s != 0.0f ? quant_pack(v[i], R) : (u32x2){0u, 0u};
             __builtin_nontemporal_store(o, qr + c);
@@ -560,12 +571,10 @@ int bs_launch_band_rowq(const uint16_t *const *parts, int P, uint8_t *q, float *
     PartPtrs pp;
     for (int p = 0; p < 16; p++) pp.p[p] = (const u32x4 *)parts[p < P ? p : 0];
     const int nch = (int)(N / 8);
-    const int64_t wg = (rows + 3) / 4;
-    if (wg > 0x7FFFFFFF || nch > 1024) return -1;
-    const dim3 grid((unsigned)wg), block(256);
-    u32x2 *qv = (u32x2 *)q;
-    if (nch <= 256) return bs_enqueue(band_rowq_kernel<4>, grid, block, stream, pp, P, qv, scale, rows, nch);
-    if (nch <= 512) return bs_enqueue(band_rowq_kernel<8>, grid, block, stream, pp, P, qv, scale, rows, nch);
-    if (nch <= 896) return bs_enqueue(band_rowq_kernel<14>, grid, block, stream, pp, P, qv, scale, rows, nch);
-    return bs_enqueue(band_rowq_kernel<16>, grid, block, stream, pp, P, qv, scale, rows, nch);
+    if (rows > 0x7FFFFFFF || nch > 256 * BRQ_CPT) return -1;
+#ifndef BRQ_G
+#define BRQ_G 4
+#endif
+    return bs_enqueue(band_rowq_kernel<BRQ_G>, dim3((unsigned)rows), dim3(256), stream, pp, P,
+                      (u32x2 *)q, scale, nch);
 }

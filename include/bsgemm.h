@@ -7,8 +7,8 @@
  *   band_reduce  fp32 sum of P bf16 partial bands into one bf16 band
  *   rowq_e4m3    per-row e4m3 quantize with one fp32 scale per row
  *   band_rowq_e4m3  band_reduce and rowq_e4m3 fused into one pass (the fused
- *                variant the pages measured and found slower; kept to
- *                reproduce that measurement)
+ *                variant the pages measured and found slower; here it is the
+ *                faster path and the one the benchmark's step runs)
  *   rowdq_e4m3   per-row e4m3 dequantize back to bf16
  *   blockq_e4m3  fp32 operand -> e4m3 codes + fp32 block scales (the
  *                activation/weight quantizer that produces bsgemm_fp8's input)
@@ -294,8 +294,11 @@ bs_status mxq_e4m3(const uint16_t *x, uint8_t *q, uint8_t *scale,
  * the bf16 band: q, scale = rowq_e4m3(band_reduce(parts)), bit for bit (the
  * fp32 part-order sum is rounded to bf16 before the row quantizer sees it).
  * [MORI] "Negative results" reports that fusing the reduce with the quantize
- * was slower than the two separate kernels, because a row's amax forces one
- * wavefront per row; this entry point reproduces that comparison.
+ * was slower than the two separate kernels, because a row's amax needs the
+ * whole row before any code can be written.  Here one workgroup takes each
+ * row with several parts' loads in flight at once, and the fused pass moves
+ * fewer bytes than the two kernels (the bf16 band is neither written nor
+ * read back), so it is the faster of the two.
  *
  *   parts  host array of P device pointers, each bf16 [rows, N] (1 <= P <= 16)
  *   q      e4m3 [rows, N];  scale  fp32 [rows]
