@@ -31,8 +31,9 @@
 //    whole 512-byte row segments of its destination band;
 //  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
-//    in groups of 8 M-tiles so that concurrently running tiles share A and B
-//    panels in that XCD's L2.
+//    in groups of 4 M-tiles so that concurrently running tiles share A and B
+//    panels in that XCD's L2 (its 32 concurrent tiles span 4 M-tiles x 8
+//    N-tiles; measured faster than 8 x 4, 2 x 16 or 1 x 32).
 //
 // A second blockscale kernel reads B in a prepacked form (the same bytes in the
 // MFMA's operand order, written once by bprepack_kernel) straight into
@@ -55,7 +56,7 @@ constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int NTHREADS = 512;
 constexpr int WM = 128, WN = 64;        // wave tile
 constexpr int TM = WM / 16, TN = WN / 16;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;
 constexpr int NUM_XCD = 8;
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -99,12 +100,13 @@ template <int ST> __device__ __forceinline__ float *stS() { return ST ? sS1 : sS
 
 // Byte offset of 16-byte chunk `c` (0..7) of tile row `r` inside a staged
 // [rows x 128 B] operand tile.  An MFMA fragment read (ds_read_b128) has each
-// 16-lane quarter read one chunk of 16 consecutive rows, and the LDS serves
-// such a quarter in one pass only when lanes 0-7 fall in the lower 128 bytes
-// of the bank array (banks 0-31) and lanes 8-15 in the upper 128 bytes, each
-// half without conflicts.  So within every 16-row group, rows 0-7 go to the
-// even 128-byte slots and rows 8-15 to the odd ones, and chunks are
-// XOR-swizzled by the row's low three bits.
+// 16-lane quarter read one chunk of 16 consecutive rows.  Within every 16-row
+// group, rows 0-7 go to the even 128-byte slots and rows 8-15 to the odd
+// ones, and chunks are XOR-swizzled by the row's low three bits: lanes 0-7 of
+// a quarter then read banks 0-31 and lanes 8-15 banks 32-63, each half
+// without conflicts, each lane from a different slot row.  Measured, this
+// reads at the LDS's full rate; the plain row-major XOR swizzle, which also
+// puts the 16 lanes in 64 distinct banks, reads at about half of it.
 __device__ __forceinline__ int lds_slot(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return lds_slot(r) * 128 + ((c ^ (r & 7)) << 4); }
 
