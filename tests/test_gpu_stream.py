@@ -184,10 +184,13 @@ def test_actq_matches_blockq():
     assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
 
 
-@pytest.mark.parametrize("rows,N,P", [(2048, 7168, 8), (37, 104, 3), (5, 8, 1), (130, 8192, 16), (64, 2048, 8)])
+@pytest.mark.parametrize("rows,N,P", [(2048, 7168, 8), (37, 104, 3), (5, 8, 1), (130, 8192, 16), (64, 2048, 8),
+                                      (300, 7168, 5), (17, 1024, 13), (2048, 7168, 7), (9, 2056, 6)])
 def test_band_rowq_bitexact(rows, N, P):
     """The fused reduce + row quantize equals the oracle's row quantize of its
-    band reduce, and the device's two separate kernels, bit for bit."""
+    band reduce, and the device's two separate kernels, bit for bit.  The
+    kernel reads the parts four at a time, so P = 5, 6, 7, 13 end on a partial
+    group; N = 2056 gives one lane a pack past the first 256."""
     say(f"band_rowq_e4m3 rows={rows} N={N} P={P}")
     parts = synth.partial_bands(rows, N, P=P, seed0=300)
     parts[0][min(2, rows - 1)] = 0                    # a zero row in one part only
