@@ -44,7 +44,8 @@
  *             shape [M,7168], K=2048), "Where the time goes" (reduce /
  *             quantize / dequantize phases), "The fp8 wire" (e4m3 with one
  *             fp32 scale per row; the reduce accumulates in fp32 and outputs
- *             bf16), "Negative results" (reduce and quantize kept separate).
+ *             bf16), "Negative results" (the pages keep reduce and quantize
+ *             as separate kernels; band_rowq_e4m3 fuses them).
  *
  * Conventions shared by every call:
  *  - All data pointers are DEVICE memory owned by the caller (the library
