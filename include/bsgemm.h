@@ -304,9 +304,9 @@ bs_status mxq_e4m3(const uint16_t *x, uint8_t *q, uint8_t *scale,
  *   parts  host array of P device pointers, each bf16 [rows, N] (1 <= P <= 16)
  *   q      e4m3 [rows, N];  scale  fp32 [rows]
  *
- * Requirements: rows >= 0; N > 0, N % 8 == 0, N <= 8192; parts and q 16-byte
- * aligned, scale 4-byte aligned; no output overlaps a part or the other
- * output.
+ * Requirements: 0 <= rows < 2^31 (one workgroup per row); N > 0, N % 8 == 0,
+ * N <= 8192; parts and q 16-byte aligned, scale 4-byte aligned; no output
+ * overlaps a part or the other output.
  */
 bs_status band_rowq_e4m3(const uint16_t *const *parts, int32_t P, uint8_t *q,
                          float *scale, int64_t rows, int64_t N, void *stream);

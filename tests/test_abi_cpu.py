@@ -191,6 +191,7 @@ def test_band_rowq_rejections(L):
     assert f(parts, 4, Q, S, -1, 1024, None) == INV and f(parts, 4, Q, S, 64, 0, None) == INV
     assert f(parts, 4, Q, S, 64, 1020, None) == UNS                 # N % 8
     assert f(parts, 4, Q, S, 64, 8200, None) == UNS                 # N > 8192
+    assert f(parts, 4, Q, S, 1 << 31, 8, None) == UNS               # one workgroup per row: rows < 2^31
     assert f(parts, 4, Q + 8, S, 64, 1024, None) == UNS and f(parts, 4, Q, S + 2, 64, 1024, None) == UNS
     assert f(parts, 4, P + 4096, S, 64, 1024, None) == INV          # q over part 0
     assert f(parts, 4, Q, Q + 1024, 64, 1024, None) == INV          # scale over q
