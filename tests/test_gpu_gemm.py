@@ -46,6 +46,7 @@ def run(qa, sa, qb, sb, bands=1, band_stride=0, C=None):
     (300, 384, 384, False),     # M not a multiple of 128
     (16, 128, 128, False),      # a single partial tile
     (513, 1024, 1152, True),    # 9 K blocks (odd count), ragged by one row
+    (1500, 2304, 512, True),    # 6 x 9 tiles: a full group of 4 M-tiles and a partial one
 ])
 def test_gemm_full_vs_oracle(M, N, K, heavy):
     say(f"bsgemm_fp8 M={M} N={N} K={K} heavy={heavy}")
