@@ -28,7 +28,8 @@
 //    values are DMA'd into LDS with the operands; each wave forms its rows'
 //    combined scales a_scale * b_scale in registers;
 //  - the bf16 tile is staged in LDS at the end so that every store writes
-//    whole 512-byte row segments of its destination band;
+//    whole 512-byte row segments of its destination band (non-temporal
+//    stores in the blockscale kernels);
 //  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
 //    in groups of 4 M-tiles so that concurrently running tiles share A and B
@@ -683,7 +684,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
             rr = rr % br;
         }
         uint16_t *crow = g.C + (int64_t)d * g.band_stride + (int64_t)rr * g.N;
-        *(u32x4 *)(crow + n) = v;
+        // C is written once.  Inside the wo_b step, storing it non-temporally
+        // made both the blockscale GEMM and the fused reduce that follows it
+        // faster (step 338 -> 331 us); the mxfp8 GEMM, measured on its own,
+        // was slower with it (162 -> 167 us) and keeps ordinary stores.
+        if constexpr (MODE == MODE_MX) *(u32x4 *)(crow + n) = v;
+        else __builtin_nontemporal_store(v, (u32x4 *)(crow + n));
     }
 }
 
