@@ -572,9 +572,9 @@ int bs_launch_band_rowq(const uint16_t *const *parts, int P, uint8_t *q, float *
     for (int p = 0; p < 16; p++) pp.p[p] = (const u32x4 *)parts[p < P ? p : 0];
     const int nch = (int)(N / 8);
     if (rows > 0x7FFFFFFF || nch > 256 * BRQ_CPT) return -1;
-#ifndef BRQ_G
-#define BRQ_G 4
-#endif
-    return bs_enqueue(band_rowq_kernel<BRQ_G>, dim3((unsigned)rows), dim3(256), stream, pp, P,
+    // parts per load group: 4 measured fastest at P = 8, [2048, 7168]
+    // (42.2 us against 43.7 for 2 and 43.1 for 8)
+    constexpr int G = 4;
+    return bs_enqueue(band_rowq_kernel<G>, dim3((unsigned)rows), dim3(256), stream, pp, P,
                       (u32x2 *)q, scale, nch);
 }
