@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 SPIN_CYCLES = 200_000_000   # ~0.1 s of torch's spin kernel
 
 
-def small_step(M=1024, N=512, K=512, bands=8):
+def small_step(M=1024, N=512, K=512, bands=8, fused=False):
     band_rows = M // bands
     A, B = synth.operand_fp32(M, N, K, seed=4, heavy=True)
     qa, sa = oracle.quant_blocks(A, 1, 128)
@@ -26,12 +26,13 @@ def small_step(M=1024, N=512, K=512, bands=8):
     parts = synth.partial_bands(band_rows, N, P=bands, seed0=100)[1:]
     wq, ws = oracle.rowq(synth.wire_rows(M, N, seed=200))
     return WoBStep(to_dev(qa), to_dev(sa), to_dev(qb), to_dev(sb), [bf16_dev(p) for p in parts],
-                   to_dev(wq), to_dev(ws), bands)
+                   to_dev(wq), to_dev(ws), bands, fused=fused)
 
 
 def outputs(step):
-    return [bits16(step.C), bits16(step.reduced), step.own_q.cpu().numpy(),
-            step.own_s.cpu().numpy().view(np.uint32), bits16(step.out)]
+    reduced = [] if step.reduced is None else [bits16(step.reduced)]
+    return [bits16(step.C)] + reduced + [step.own_q.cpu().numpy(),
+                                         step.own_s.cpu().numpy().view(np.uint32), bits16(step.out)]
 
 
 def test_calls_follow_their_stream():
@@ -60,13 +61,15 @@ def test_calls_follow_their_stream():
         assert np.array_equal(g, w)
 
 
-def test_step_graph_capture_and_replay():
-    """The whole step captured into a graph on a side stream and replayed three
-    times, with eager work on the same buffers between replays; every replay
-    equals the eager result."""
+@pytest.mark.parametrize("fused", [False, True])
+def test_step_graph_capture_and_replay(fused):
+    """The whole step (split, or with the fused reduce + quantize the benchmark
+    runs) captured into a graph on a side stream and replayed three times, with
+    eager work on the same buffers between replays; every replay equals the
+    eager result."""
     dev = device()
-    say("graph capture of the step")
-    step = small_step()
+    say(f"graph capture of the step (fused={fused})")
+    step = small_step(fused=fused)
     step.step()
     torch.cuda.synchronize()
     want = outputs(step)
@@ -83,7 +86,8 @@ def test_step_graph_capture_and_replay():
     torch.cuda.synchronize()
     for r in range(3):
         poison_bf16(step.C)
-        poison_bf16(step.reduced)
+        if step.reduced is not None:
+            poison_bf16(step.reduced)
         poison_bf16(step.out)
         step.own_q.fill_(0x7F)
         torch.cuda.synchronize()
