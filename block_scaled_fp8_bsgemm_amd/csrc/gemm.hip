@@ -474,14 +474,18 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
     a = a_next;
 }
 
-static_assert(64 * BN * 2 == BM * BK, "each operand array holds 64 rows of the bf16 output tile");
+static_assert(2 * WM * WN * 2 == BM * BK, "each operand array holds two waves' bf16 sub-tiles");
 
-// Row ml (0..255) of the bf16 output tile staged in LDS: 64 rows in each of
-// the four operand arrays, 512 bytes per row.
-__device__ __forceinline__ uint8_t *out_row(int ml) {
-    const int q = ml >> 6;
+// Wave w's private 16 KiB for staging its 128 x 64 bf16 sub-tile: half of
+// one operand array, 128-byte rows, the four 32-byte units of a row rotated
+// by bits 1-2 of the row so that a fragment's 16 rows spread over all banks.
+__device__ __forceinline__ uint8_t *stage_base(int wave) {
+    const int q = wave >> 1;
     uint8_t *base = q == 0 ? sA0 : q == 1 ? sA1 : q == 2 ? sB0 : sB1;
-    return base + (ml & 63) * (BN * 2);
+    return base + (wave & 1) * (WM * WN * 2);
+}
+__device__ __forceinline__ int stage_off(int lr, int byte) {
+    return lr * (WN * 2) + (byte ^ (((lr >> 1) & 3) << 5));
 }
 
 // One 256x256 output tile.  MODE_BS: blockscale operands, A and B staged in
@@ -642,54 +646,71 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last (empty) DMA is retired
 
     // ---- epilogue ----
-    // The bf16 tile is staged in LDS (the four operand arrays, 64 rows each,
-    // 512 B per row, 32-byte units XOR-swizzled by row) so that the global
-    // stores write whole 512-byte row segments: each store instruction
-    // covers two rows, lane l the 16 bytes at column 8 * (l % 32).
-    __syncthreads();   // every wave is done with the operand stages
+    // Each wave stages its own 128 x 64 bf16 sub-tile in a private LDS region
+    // and stores it back as 128-byte row segments, eight rows per store
+    // instruction.  No workgroup barrier is needed: after the last K block's
+    // barrier nobody reads the operand stages again (the head reads of the
+    // nonexistent next block fetch values that are never used), and a wave's
+    // own LDS writes are complete once lgkmcnt reaches zero.
+    uint8_t *stg = stage_base(wave);
 #pragma unroll
     for (int i = 0; i < TM; i++) {
-        const int ml = wm * WM + i * 16 + frow;
-        uint8_t *row = out_row(ml);
+        const int lr = i * 16 + frow;
 #pragma unroll
         for (int j = 0; j < TN; j++) {
-            const int byte = (wn * WN + j * 16 + (lane >> 4) * 4) * 2;
             uint2 w;
             w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
             w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            *(uint2 *)(row + (byte ^ ((ml & 15) << 5))) = w;
+            *(uint2 *)(stg + stage_off(lr, j * 32 + (lane >> 4) * 8)) = w;
         }
     }
-    __syncthreads();
-    const int64_t n = n0 + (lane & 31) * 8;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    // Store r covers sub-tile rows 8r .. 8r+7; lane l the 16 bytes at column
+    // 8 * (l % 8) of row 8r + l / 8.
+    constexpr int RPW = WM / 8;   // store instructions per wave
+    u32x4 vrow[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; r++)
+        vrow[r] = *(const u32x4 *)(stg + stage_off(r * 8 + (lane >> 3), (lane & 7) * 16));
+#pragma unroll
+    for (int r = 0; r < RPW; r++) asm volatile("" : "+v"(vrow[r]));
+
+    const int64_t n = n0 + wn * WN + (lane & 7) * 8;
     // Row m0 + ml lies in band d0 + (r0 + ml) / band_rows at row (r0 + ml) %
     // band_rows, with d0, r0 those of the tile's first row (rows < 2^31): one
-    // division per tile; with bands of at least 256 rows a tile row crosses at
-    // most one band boundary, so a compare replaces the per-row division.
+    // division per tile.  With bands of at least 256 rows a tile crosses at
+    // most one band boundary, at tile row mlb: rows before it are at element
+    // off0 + ml * N of C, rows from it on at off1 + ml * N, so each stored row
+    // costs a compare, a select and an add.
     const uint32_t br = (uint32_t)g.band_rows;
     const uint32_t d0 = __builtin_amdgcn_readfirstlane((uint32_t)m0 / br);
     const uint32_t r0 = (uint32_t)m0 - d0 * br;
+    const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);   // tile rows inside M
+    const bool col_ok = n < g.N;
+    const int ml0 = wm * WM + (lane >> 3);
+    const int64_t lane_off = (int64_t)ml0 * g.N + n;
+    const int64_t off0 = (int64_t)d0 * g.band_stride + (int64_t)r0 * g.N;
+    const int64_t off1 = (int64_t)(d0 + 1) * g.band_stride - (int64_t)(br - r0) * g.N;
+    const int mlb = br - r0 < (uint32_t)BM ? (int)(br - r0) : BM;
 #pragma unroll
-    for (int r = 0; r < BM / 8 / 2; r++) {
-        const int ml = wave * (BM / 8) + r * 2 + (lane >> 5);
-        const u32x4 v = *(const u32x4 *)(out_row(ml) + (((lane & 31) * 16) ^ ((ml & 15) << 5)));
-        if (m0 + ml >= g.M || n >= g.N) continue;
-        uint32_t rr = r0 + (uint32_t)ml, d = d0;
+    for (int r = 0; r < RPW; r++) {
+        const int ml = ml0 + r * 8;
+        const u32x4 v = vrow[r];
+        if (ml >= rows || !col_ok) continue;
+        uint16_t *dst;
         if (br >= BM) {
-            const bool carry = rr >= br;
-            rr = carry ? rr - br : rr;
-            d = carry ? d + 1 : d;
+            dst = g.C + ((ml < mlb ? off0 : off1) + lane_off + (int64_t)(r * 8) * g.N);
         } else {
-            d += rr / br;
-            rr = rr % br;
+            const uint32_t rr = r0 + (uint32_t)ml;
+            dst = g.C + ((int64_t)(d0 + rr / br) * g.band_stride + (int64_t)(rr % br) * g.N + n);
         }
-        uint16_t *crow = g.C + (int64_t)d * g.band_stride + (int64_t)rr * g.N;
         // C is written once.  Inside the wo_b step, storing it non-temporally
         // made both the blockscale GEMM and the fused reduce that follows it
         // faster (step 338 -> 331 us); the mxfp8 GEMM, measured on its own,
         // was slower with it (162 -> 167 us) and keeps ordinary stores.
-        if constexpr (MODE == MODE_MX) *(u32x4 *)(crow + n) = v;
-        else __builtin_nontemporal_store(v, (u32x4 *)(crow + n));
+        if constexpr (MODE == MODE_MX) *(u32x4 *)dst = v;
+        else __builtin_nontemporal_store(v, (u32x4 *)dst);
     }
 }
 
