@@ -27,14 +27,21 @@
 //  - the K block's a_scale values of the tile's 256 rows and its b_scale
 //    values are DMA'd into LDS with the operands; each wave forms its rows'
 //    combined scales a_scale * b_scale in registers;
-//  - the bf16 tile is staged in LDS at the end so that every store writes
-//    whole 512-byte row segments of its destination band (non-temporal
-//    stores in the blockscale kernels);
+//  - at the end each wave stages its 128 x 64 bf16 sub-tile in LDS of its
+//    own and stores it as whole 128-byte row segments of the destination
+//    band, eight rows per instruction, with no workgroup barrier
+//    (non-temporal stores in the blockscale kernels);
 //  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
 //    in groups of 4 M-tiles so that concurrently running tiles share A and B
 //    panels in that XCD's L2 (its 32 concurrent tiles span 4 M-tiles x 8
 //    N-tiles; measured faster than 8 x 4, 2 x 16 or 1 x 32).
+//
+// When K / 128 is even (the benchmark's K = 2048), the blockscale GEMM runs
+// as a persistent kernel instead: one workgroup per CU walks several tiles,
+// and the next tile's first K block is DMA'd while the finished tile's
+// epilogue runs, so that neither the workgroup launch nor the first block's
+// load latency is paid per tile (bit-identical results).
 //
 // A second blockscale kernel reads B in a prepacked form (the same bytes in the
 // MFMA's operand order, written once by bprepack_kernel) straight into
@@ -111,13 +118,26 @@ template <int ST> __device__ __forceinline__ float *stS() { return ST ? sS1 : sS
 __device__ __forceinline__ int lds_slot(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return lds_slot(r) * 128 + ((c ^ (r & 7)) << 4); }
 
+// Every descriptor here is workgroup-uniform; readfirstlane says so to the
+// compiler, which otherwise may keep one in VGPRs and wrap each load through
+// it in a loop over distinct values.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, int64_t bytes) {
     int32_t n = bytes > 0x7FFFFFFFll ? 0x7FFFFFFF : (bytes > 0 ? (int32_t)bytes : 0);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
+    const uint64_t b = (uint64_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    n = __builtin_amdgcn_readfirstlane(n);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                             0x00020000);
 }
 
-struct Loader {
+// A tile's operand descriptors: its row panels of A and B, and its scales.
+struct Panels {
     __amdgpu_buffer_rsrc_t rA, rB, rS;   // rS: a_scale (waves 0..3) or b_scale (4..7)
+};
+
+struct Loader {
+    Panels P;                            // the current tile's
     __amdgpu_buffer_rsrc_t rZ;           // zero-size: every load through it reads nothing
     int poff;    // prepacked B: this lane's byte offset in its wave's first fragment
     int pstep;   // prepacked B: bytes from one 16-row group to the next (K/128 * 2 KiB)
@@ -134,7 +154,7 @@ struct Loader {
 // past the end (valid == false) goes through the zero-size descriptor: the
 // loads touch no memory and the stage is not read again.
 template <int ST, int PIECE>
-__device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
+__device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int kb, bool valid) {
     const int koff = kb * BK;
     if (PIECE < 8) {
         const int i = PIECE >> 1;
@@ -142,10 +162,10 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
         // slot i's rows are those of slot 0 plus 0, 4, 16, 20 (see load_stage)
         const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4;
         if (PIECE & 1)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rB : L.rZ, (lds_void *)(stB<ST>() + q),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rB : L.rZ, (lds_void *)(stB<ST>() + q),
                                                      16, vo, koff, 0, 0);
         else
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rA : L.rZ, (lds_void *)(stA<ST>() + q),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rA : L.rZ, (lds_void *)(stA<ST>() + q),
                                                      16, vo, koff, 0, 0);
     } else {
         // blockscale: waves 0..3 fetch a_scale of rows 64w..64w+63, waves
@@ -153,7 +173,7 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
         // mxfp8: waves 0..3 fetch the 4 scale bytes of the K block for A rows
         // 64w.., waves 4..7 for B rows 64(w-4)..  Each wave fills its own
         // 256-byte slot; no branch: every wave issues exactly one.
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? L.rS : L.rZ,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rS : L.rZ,
                                                  (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
                                                  L.soff, kb * 4, 0, 0);
     }
@@ -169,11 +189,11 @@ __device__ __forceinline__ void dma_piece(const Loader &L, int kb, bool valid) {
 // swizzle.
 template <int ST>
 __device__ __forceinline__ void load_stage(const Loader &L, int kb, bool valid = true) {
-    dma_piece<ST, 0>(L, kb, valid); dma_piece<ST, 1>(L, kb, valid);
-    dma_piece<ST, 2>(L, kb, valid); dma_piece<ST, 3>(L, kb, valid);
-    dma_piece<ST, 4>(L, kb, valid); dma_piece<ST, 5>(L, kb, valid);
-    dma_piece<ST, 6>(L, kb, valid); dma_piece<ST, 7>(L, kb, valid);
-    dma_piece<ST, 8>(L, kb, valid);
+    dma_piece<ST, 0>(L, L.P, kb, valid); dma_piece<ST, 1>(L, L.P, kb, valid);
+    dma_piece<ST, 2>(L, L.P, kb, valid); dma_piece<ST, 3>(L, L.P, kb, valid);
+    dma_piece<ST, 4>(L, L.P, kb, valid); dma_piece<ST, 5>(L, L.P, kb, valid);
+    dma_piece<ST, 6>(L, L.P, kb, valid); dma_piece<ST, 7>(L, L.P, kb, valid);
+    dma_piece<ST, 8>(L, L.P, kb, valid);
 }
 
 __device__ __forceinline__ v8i lds_frag(const uint8_t *st, int r, int fc) {
@@ -266,20 +286,25 @@ __device__ __forceinline__ void read_head_mx(v8i &a, v8i (&bf)[TN], MxScales &x,
 
 // DMA of block kb + 1 into stage ST ^ 1 during the first nine MFMAs of block
 // kb (see kblock).
+// (The persistent kernel passes the next tile's descriptors and block 0 in
+// the last K block of a tile: dma_block takes them explicitly.)
+template <int ST>
+__device__ __forceinline__ void dma_block(const Loader &L, const Panels &P, int k, int kload, bool v) {
+    if (k < 9) {
+        if (k == 0) dma_piece<ST ^ 1, 8>(L, P, kload, v);
+        if (k == 1) dma_piece<ST ^ 1, 0>(L, P, kload, v);
+        if (k == 2) dma_piece<ST ^ 1, 1>(L, P, kload, v);
+        if (k == 3) dma_piece<ST ^ 1, 2>(L, P, kload, v);
+        if (k == 4) dma_piece<ST ^ 1, 3>(L, P, kload, v);
+        if (k == 5) dma_piece<ST ^ 1, 4>(L, P, kload, v);
+        if (k == 6) dma_piece<ST ^ 1, 5>(L, P, kload, v);
+        if (k == 7) dma_piece<ST ^ 1, 6>(L, P, kload, v);
+        if (k == 8) dma_piece<ST ^ 1, 7>(L, P, kload, v);
+    }
+}
 template <int ST>
 __device__ __forceinline__ void dma_next(const Loader &L, int k, int kb, int KB) {
-    if (k < 9) {
-        const bool v = kb + 1 < KB;
-        if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
-        if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
-        if (k == 2) dma_piece<ST ^ 1, 1>(L, kb + 1, v);
-        if (k == 3) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
-        if (k == 4) dma_piece<ST ^ 1, 3>(L, kb + 1, v);
-        if (k == 5) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
-        if (k == 6) dma_piece<ST ^ 1, 5>(L, kb + 1, v);
-        if (k == 7) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
-        if (k == 8) dma_piece<ST ^ 1, 7>(L, kb + 1, v);
-    }
+    dma_block<ST>(L, L.P, k, kb + 1, kb + 1 < KB);
 }
 
 // One mxfp8 K block from stage ST: the same schedule as the blockscale kblock
@@ -328,7 +353,7 @@ __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[
 // descriptor.
 template <int H>
 __device__ __forceinline__ void load_bp_half(const Loader &L, v8i &f, int j, int kb, bool valid) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(valid ? L.rB : L.rZ, L.poff + H * 1024,
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(valid ? L.P.rB : L.rZ, L.poff + H * 1024,
                                                           j * L.pstep + kb * 2048, 0);
 #pragma unroll
     for (int e = 0; e < 4; e++) f[4 * H + e] = (int)v[e];
@@ -345,20 +370,20 @@ __device__ __forceinline__ void load_next_pb(const Loader &L, v8i (&bn)[TN], int
         if (k & 1) load_bp_half<1>(L, bn[k >> 1], k >> 1, kb + 1, v);
         else load_bp_half<0>(L, bn[k >> 1], k >> 1, kb + 1, v);
     }
-    if (k == 0) dma_piece<ST ^ 1, 8>(L, kb + 1, v);
-    if (k == 1) dma_piece<ST ^ 1, 0>(L, kb + 1, v);
-    if (k == 2) dma_piece<ST ^ 1, 2>(L, kb + 1, v);
-    if (k == 3) dma_piece<ST ^ 1, 4>(L, kb + 1, v);
-    if (k == 4) dma_piece<ST ^ 1, 6>(L, kb + 1, v);
+    if (k == 0) dma_piece<ST ^ 1, 8>(L, L.P, kb + 1, v);
+    if (k == 1) dma_piece<ST ^ 1, 0>(L, L.P, kb + 1, v);
+    if (k == 2) dma_piece<ST ^ 1, 2>(L, L.P, kb + 1, v);
+    if (k == 3) dma_piece<ST ^ 1, 4>(L, L.P, kb + 1, v);
+    if (k == 4) dma_piece<ST ^ 1, 6>(L, L.P, kb + 1, v);
 }
 
 // The first K block of a tile: A slots and scales by DMA into stage ST, the
 // B fragments into b; then the head reads (A row group 0, the scales).
 template <int ST>
 __device__ __forceinline__ void load_first_pb(const Loader &L, v8i (&b)[TN]) {
-    dma_piece<ST, 8>(L, 0, true);
-    dma_piece<ST, 0>(L, 0, true); dma_piece<ST, 2>(L, 0, true);
-    dma_piece<ST, 4>(L, 0, true); dma_piece<ST, 6>(L, 0, true);
+    dma_piece<ST, 8>(L, L.P, 0, true);
+    dma_piece<ST, 0>(L, L.P, 0, true); dma_piece<ST, 2>(L, L.P, 0, true);
+    dma_piece<ST, 4>(L, L.P, 0, true); dma_piece<ST, 6>(L, L.P, 0, true);
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         load_bp_half<0>(L, b[j], j, 0, true);
@@ -432,8 +457,9 @@ __device__ __forceinline__ void kblock_pb(v4f (&acc)[TM][TN], v4f (&p)[4], float
 // values.
 template <int ST>
 __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
-                                       v8i (&bf)[TN], float (&s)[TM], const Loader &L, int kb,
-                                       int KB, int wm, int wn, int frow, int fc) {
+                                       v8i (&bf)[TN], float (&s)[TM], const Loader &L,
+                                       const Panels &P, int kload, bool vload, int wm, int wn,
+                                       int frow, int fc) {
     const uint8_t *as = stA<ST>();
     v8i an = a;
     v8i a_next = a;
@@ -462,10 +488,12 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             if (i == TM - 1) {
                 bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
             }
-            // the DMA of block kb + 1 into the other stage (unread since the
-            // previous block's barrier), one instruction after each of the
-            // first nine MFMAs, away from the head reads of row group 7
-            dma_next<ST>(L, k, kb, KB);
+            // the DMA of the next block (kb + 1, or in the persistent kernel's
+            // last block of a tile the next tile's block 0) into the other
+            // stage (unread since the previous block's barrier), one
+            // instruction after each of the first nine MFMAs, away from the
+            // head reads of row group 7
+            dma_block<ST>(L, P, k, kload, vload);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -488,66 +516,138 @@ __device__ __forceinline__ int stage_off(int lr, int byte) {
     return lr * (WN * 2) + (byte ^ (((lr >> 1) & 3) << 5));
 }
 
-// One 256x256 output tile.  MODE_BS: blockscale operands, A and B staged in
-// LDS; MODE_PB: blockscale with the prepacked B loaded into registers;
-// MODE_MX: mxfp8 operands (E8M0 scales per 1x32 block, applied by the scaled
-// MFMA).
 constexpr int MODE_BS = 0, MODE_PB = 1, MODE_MX = 2;
-template <int MODE>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
-    // ---- workgroup -> tile (XCD-aware, grouped) ----
+
+// Workgroup (or, in the persistent kernel, virtual workgroup) b -> tile,
+// XCD-aware and grouped: b runs on XCD b % 8, which is given the contiguous
+// run of tiles [x * per_xcd, (x + 1) * per_xcd), ordered in groups of GROUP_M
+// M-tiles.  False for the padding workgroups past the last tile.
+__device__ __forceinline__ bool tile_of(const GemmArgs &g, int b, int64_t &m0, int64_t &n0) {
     const int T = g.tiles_m * g.tiles_n;
     const int per_xcd = (T + NUM_XCD - 1) / NUM_XCD;
-    const int b = blockIdx.x;
+    if (b >= per_xcd * NUM_XCD) return false;
     const int t = (b % NUM_XCD) * per_xcd + b / NUM_XCD;
-    if (t >= T) return;
+    if (t >= T) return false;
     const int group = t / (GROUP_M * g.tiles_n);
     const int first_m = group * GROUP_M;
     const int gm = min(GROUP_M, g.tiles_m - first_m);
     const int local = t - group * GROUP_M * g.tiles_n;
-    const int tm = first_m + local % gm;
-    const int tn = local / gm;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    m0 = (int64_t)(first_m + local % gm) * BM;
+    n0 = (int64_t)(local / gm) * BN;
+    return true;
+}
+
+// The tile-dependent part of the loader: descriptors of the tile's row panels
+// and scales, zero past the end of the matrices.
+template <int MODE>
+__device__ __forceinline__ Panels panels_of(const GemmArgs &g, int64_t m0, int64_t n0, int wave) {
+    const int64_t K = g.K;
+    Panels P;
+    P.rA = make_rsrc(g.A + m0 * K, (g.M - m0) * K);
+    if (MODE == MODE_PB)
+        P.rB = make_rsrc(g.B + (n0 / 16) * ((int64_t)g.KB * 2048), (g.N - n0) * K);
+    else
+        P.rB = make_rsrc(g.B + n0 * K, (g.N - n0) * K);
+    if (MODE == MODE_MX) {
+        const int KQ = (int)(K / 32);   // mxfp8 scale bytes per row
+        P.rS = wave < 4 ? make_rsrc((const uint8_t *)g.sa + m0 * KQ, (g.M - m0) * KQ)
+                        : make_rsrc((const uint8_t *)g.sb + n0 * KQ, (g.N - n0) * KQ);
+    } else {
+        const int nb0 = (int)(n0 / 128);
+        P.rS = wave < 4 ? make_rsrc((const float *)g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
+                        : make_rsrc((const float *)g.sb + (int64_t)nb0 * g.KB,
+                                    (int64_t)(g.NB - nb0) * g.KB * 4);
+    }
+    return P;
+}
+
+// The lane-dependent part, the same for every tile.
+template <int MODE>
+__device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wave, int lane) {
+    const int K = (int)g.K;
+    L.rZ = make_rsrc(g.A, 0);
+    L.ldsq = wave * 4096;
+    if (MODE == MODE_PB) {
+        L.pstep = g.KB * 2048;
+        L.poff = (wave & 3) * TN * L.pstep + lane * 16;
+    }
+    // slot 0's row and chunk of this lane (see load_stage); the odd slots'
+    // rows are 4 further on, so their row & 7 has bit 2 set
+    const int row = wave * 32 + (lane >> 4) + 8 * ((lane >> 3) & 1);
+    const int chunk = (lane & 7) ^ (lane >> 4);
+    L.voff = row * K + chunk * 16;
+    L.voff1 = L.voff ^ 64;
+    L.k4 = 4 * K;
+    L.soff = MODE == MODE_MX ? ((wave & 3) * 64 + lane) * (K / 32)
+                             : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
+    L.sdst = wave * 256;
+}
+
+// Where the epilogue's stores go.  Row m0 + ml of a tile lies in band
+// d0 + (r0 + ml) / band_rows at row (r0 + ml) % band_rows, with d0, r0 those
+// of the tile's first row (rows < 2^31): one division per tile.  With bands
+// of at least 256 rows a tile crosses at most one band boundary, at tile row
+// mlb: rows before it are at element off0 + ml * N of C, rows from it on at
+// off1 + ml * N, so each stored row costs a compare, a select and an add.
+struct BandOut {
+    int64_t off0, off1, lane_off, n;
+    uint32_t br, d0, r0;
+    int mlb, rows, ml0;
+    bool col_ok;
+};
+__device__ __forceinline__ BandOut band_out(const GemmArgs &g, int64_t m0, int64_t n, int ml0) {
+    BandOut o;
+    o.n = n;
+    o.ml0 = ml0;
+    o.br = (uint32_t)g.band_rows;
+    o.d0 = __builtin_amdgcn_readfirstlane((uint32_t)m0 / o.br);
+    o.r0 = (uint32_t)m0 - o.d0 * o.br;
+    o.rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);   // tile rows inside M
+    o.col_ok = n < g.N;
+    o.lane_off = (int64_t)ml0 * g.N + n;
+    o.off0 = (int64_t)o.d0 * g.band_stride + (int64_t)o.r0 * g.N;
+    o.off1 = (int64_t)(o.d0 + 1) * g.band_stride - (int64_t)(o.br - o.r0) * g.N;
+    o.mlb = o.br - o.r0 < (uint32_t)BM ? (int)(o.br - o.r0) : BM;
+    return o;
+}
+// Store one 16-byte piece of tile row ml = o.ml0 + dml (dml a constant).
+template <int MODE>
+__device__ __forceinline__ void band_store(const GemmArgs &g, const BandOut &o, int dml, u32x4 v) {
+    const int ml = o.ml0 + dml;
+    if (ml >= o.rows || !o.col_ok) return;
+    uint16_t *dst;
+    if (o.br >= BM) {
+        dst = g.C + ((ml < o.mlb ? o.off0 : o.off1) + o.lane_off + (int64_t)dml * g.N);
+    } else {
+        const uint32_t rr = o.r0 + (uint32_t)ml;
+        dst = g.C + ((int64_t)(o.d0 + rr / o.br) * g.band_stride + (int64_t)(rr % o.br) * g.N + o.n);
+    }
+    // C is written once.  Inside the wo_b step, storing it non-temporally
+    // made both the blockscale GEMM and the fused reduce that follows it
+    // faster (step 338 -> 331 us); the mxfp8 GEMM, measured on its own,
+    // was slower with it (162 -> 167 us) and keeps ordinary stores.
+    if constexpr (MODE == MODE_MX) *(u32x4 *)dst = v;
+    else __builtin_nontemporal_store(v, (u32x4 *)dst);
+}
+
+// One 256x256 output tile.  MODE_BS: blockscale operands, A and B staged in
+// LDS; MODE_PB: blockscale with the prepacked B loaded into registers;
+// MODE_MX: mxfp8 operands (E8M0 scales per 1x32 block, applied by the scaled
+// MFMA).
+template <int MODE>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
+    int64_t m0, n0;
+    if (!tile_of(g, blockIdx.x, m0, n0)) return;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
     const int wm = wave >> 2, wn = wave & 3;
-    const int64_t K = g.K;
     const int KB = g.KB;
-
-    // ---- operand descriptors: this tile's row panels, zero past the end ----
-    Loader L;
-    L.rA = make_rsrc(g.A + m0 * K, (g.M - m0) * K);
-    L.rB = make_rsrc(g.B + n0 * K, (g.N - n0) * K);
-    const int KQ = (int)(K / 32);   // mxfp8 scale bytes per row
     constexpr bool MX = MODE == MODE_MX;
-    if (MODE == MODE_PB) {
-        L.pstep = KB * 2048;
-        L.rB = make_rsrc(g.B + (n0 / 16) * (int64_t)L.pstep, (g.N - n0) * K);
-        L.poff = wn * TN * L.pstep + lane * 16;
-    }
-    if (MX) {
-        L.rS = wave < 4 ? make_rsrc((const uint8_t *)g.sa + m0 * KQ, (g.M - m0) * KQ)
-                        : make_rsrc((const uint8_t *)g.sb + n0 * KQ, (g.N - n0) * KQ);
-    } else {
-        const int nb0 = (int)(n0 / 128);
-        L.rS = wave < 4 ? make_rsrc((const float *)g.sa + m0 * g.KB, (g.M - m0) * g.KB * 4)
-                        : make_rsrc((const float *)g.sb + (int64_t)nb0 * g.KB,
-                                    (int64_t)(g.NB - nb0) * g.KB * 4);
-    }
-    L.rZ = make_rsrc(g.A, 0);
-    L.ldsq = wave * 4096;
-    {
-        // slot 0's row and chunk of this lane (see load_stage); the odd slots'
-        // rows are 4 further on, so their row & 7 has bit 2 set
-        const int row = wave * 32 + (lane >> 4) + 8 * ((lane >> 3) & 1);
-        const int chunk = (lane & 7) ^ (lane >> 4);
-        L.voff = row * (int)K + chunk * 16;
-        L.voff1 = L.voff ^ 64;
-        L.k4 = 4 * (int)K;
-        L.soff = MX ? ((wave & 3) * 64 + lane) * KQ : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
-        L.sdst = wave * 256;
-    }
+
+    Loader L;
+    init_loader<MODE>(L, g, wave, lane);
+    L.P = panels_of<MODE>(g, m0, n0, wave);
 
     const int frow = lane & 15;
     const int fc = (lane >> 4) * 2;
@@ -633,12 +733,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
 
     int kb = 0;
     if (KB & 1) {
-        kblock<0>(acc, p, s_tail, a, bf, s, L, 0, KB, wm, wn, frow, fc);
+        kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, 1, 1 < KB, wm, wn, frow, fc);
         kb = 1;
     }
     for (; kb < KB; kb += 2) {
-        kblock<1>(acc, p, s_tail, a, bf, s, L, kb, KB, wm, wn, frow, fc);
-        kblock<0>(acc, p, s_tail, a, bf, s, L, kb + 1, KB, wm, wn, frow, fc);
+        kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, kb + 1 < KB, wm, wn, frow, fc);
+        kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
     }
 #pragma unroll
     for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
@@ -676,41 +776,149 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
 #pragma unroll
     for (int r = 0; r < RPW; r++) asm volatile("" : "+v"(vrow[r]));
 
-    const int64_t n = n0 + wn * WN + (lane & 7) * 8;
-    // Row m0 + ml lies in band d0 + (r0 + ml) / band_rows at row (r0 + ml) %
-    // band_rows, with d0, r0 those of the tile's first row (rows < 2^31): one
-    // division per tile.  With bands of at least 256 rows a tile crosses at
-    // most one band boundary, at tile row mlb: rows before it are at element
-    // off0 + ml * N of C, rows from it on at off1 + ml * N, so each stored row
-    // costs a compare, a select and an add.
-    const uint32_t br = (uint32_t)g.band_rows;
-    const uint32_t d0 = __builtin_amdgcn_readfirstlane((uint32_t)m0 / br);
-    const uint32_t r0 = (uint32_t)m0 - d0 * br;
-    const int rows = (int)(g.M - m0 < BM ? g.M - m0 : BM);   // tile rows inside M
-    const bool col_ok = n < g.N;
-    const int ml0 = wm * WM + (lane >> 3);
-    const int64_t lane_off = (int64_t)ml0 * g.N + n;
-    const int64_t off0 = (int64_t)d0 * g.band_stride + (int64_t)r0 * g.N;
-    const int64_t off1 = (int64_t)(d0 + 1) * g.band_stride - (int64_t)(br - r0) * g.N;
-    const int mlb = br - r0 < (uint32_t)BM ? (int)(br - r0) : BM;
+    const BandOut o = band_out(g, m0, n0 + wn * WN + (lane & 7) * 8, wm * WM + (lane >> 3));
 #pragma unroll
-    for (int r = 0; r < RPW; r++) {
-        const int ml = ml0 + r * 8;
-        const u32x4 v = vrow[r];
-        if (ml >= rows || !col_ok) continue;
-        uint16_t *dst;
-        if (br >= BM) {
-            dst = g.C + ((ml < mlb ? off0 : off1) + lane_off + (int64_t)(r * 8) * g.N);
-        } else {
-            const uint32_t rr = r0 + (uint32_t)ml;
-            dst = g.C + ((int64_t)(d0 + rr / br) * g.band_stride + (int64_t)(rr % br) * g.N + n);
+    for (int r = 0; r < RPW; r++) band_store<MODE>(g, o, r * 8, vrow[r]);
+}
+
+// ---- persistent blockscale kernel (K / 128 even) ----
+// One workgroup per CU walks the tiles of virtual workgroups b, b + G,
+// b + 2G, ... (G = grid size, a multiple of 8, so every tile stays on the XCD
+// the non-persistent mapping gives it).  The K blocks of successive tiles form
+// one stream.  After a tile's last K block (which always sits in stage 0)
+// the next tile's block 0 is DMA'd into stage 1, unread by then, while the
+// finished tile's epilogue runs, so the first block's load latency and the
+// workgroup launch are hidden behind the epilogue.  That epilogue has only
+// stage 0 to stage through: each wave stages its 128 x 64 bf16 sub-tile in
+// two 64-row halves in the 8 KiB its own DMAs fill (4 KiB of each operand
+// array), which no other wave touches until the next tile's first barrier;
+// no workgroup barrier is needed inside it.  (A variant that issued that DMA
+// from inside the last K block spilled registers in the K loop.)
+__device__ __forceinline__ uint8_t *pstage_row(int wave, int lr) {
+    return (lr < 32 ? sA0 : sB0) + wave * 4096 + (lr & 31) * (WN * 2);
+}
+
+__device__ __forceinline__ void store_tile_halves(const v4f (&acc)[TM][TN], const GemmArgs &g,
+                                                  int64_t m0, int64_t n0, int wave, int lane) {
+    // opaque to the compiler, so that the addresses below are formed here
+    // rather than hoisted out of the tile loop and kept live across it
+    asm volatile("" : "+v"(lane));
+    const int wm = wave >> 2, wn = wave & 3, frow = lane & 15;
+    const BandOut o = band_out(g, m0, n0 + wn * WN + (lane & 7) * 8, wm * WM + (lane >> 3));
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int i = 0; i < TM / 2; i++) {
+            const int lr = i * 16 + frow;
+            uint8_t *row = pstage_row(wave, lr);
+#pragma unroll
+            for (int j = 0; j < TN; j++) {
+                const v4f &c = acc[h * (TM / 2) + i][j];
+                uint2 w;
+                w.x = pack_bf16x2(c[0], c[1]);
+                w.y = pack_bf16x2(c[2], c[3]);
+                *(uint2 *)(row + ((j * 32 + (lane >> 4) * 8) ^ (((lr >> 1) & 3) << 5))) = w;
+            }
         }
-        // C is written once.  Inside the wo_b step, storing it non-temporally
-        // made both the blockscale GEMM and the fused reduce that follows it
-        // faster (step 338 -> 331 us); the mxfp8 GEMM, measured on its own,
-        // was slower with it (162 -> 167 us) and keeps ordinary stores.
-        if constexpr (MODE == MODE_MX) *(u32x4 *)dst = v;
-        else __builtin_nontemporal_store(v, (u32x4 *)dst);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
+        __builtin_amdgcn_wave_barrier();
+        constexpr int RPH = WM / 2 / 8;   // store instructions per half
+        u32x4 vrow[RPH];
+#pragma unroll
+        for (int r = 0; r < RPH; r++) {
+            const int lr = r * 8 + (lane >> 3);
+            vrow[r] = *(const u32x4 *)(pstage_row(wave, lr) + (((lane & 7) * 16) ^ (((lr >> 1) & 3) << 5)));
+        }
+        // the reads are complete before the next half overwrites the region
+#pragma unroll
+        for (int r = 0; r < RPH; r++) asm volatile("" : "+v"(vrow[r]));
+#pragma unroll
+        for (int r = 0; r < RPH; r++) band_store<MODE_BS>(g, o, h * (WM / 2) + r * 8, vrow[r]);
+    }
+}
+
+__global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g) {
+    int vb = blockIdx.x;
+    int64_t m0, n0;
+    if (!tile_of(g, vb, m0, n0)) return;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
+    const int wm = wave >> 2, wn = wave & 3;
+    const int KB = g.KB;   // even, at least 2
+    const int frow = lane & 15;
+    const int fc = (lane >> 4) * 2;
+
+    Loader L;
+    init_loader<MODE_BS>(L, g, wave, lane);
+    L.P = panels_of<MODE_BS>(g, m0, n0, wave);
+
+    v4f acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; i++)
+#pragma unroll
+        for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // block 0 of every tile sits in stage 1 (K / 128 even)
+    v8i a, bf[TN];
+    float s[TM];
+    load_stage<1>(L, 0);
+    wait_dma_and_sync();
+    read_head<1>(a, bf, s, wm, wn, frow, fc);
+
+    v4f p[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+    float s_tail = 0.f;
+
+    // The kernel's only argument, read in place from the kernarg segment
+    // where each tile needs it (scalar loads), rather than held in SGPRs
+    // across the K loop.
+    typedef const __attribute__((address_space(4))) GemmArgs *KArgs;
+    const KArgs gp = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
+    auto args = [gp]() {
+        KArgs q = gp;
+        asm volatile("" : "+s"(q));
+        return *(const GemmArgs *)q;
+    };
+    for (;;) {
+        for (int kb = 0; kb < KB; kb += 2) {
+            kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
+            kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
+        }
+        // the next tile's block 0 goes to stage 1 (unread after the last
+        // block's barrier but for head reads whose values are never used)
+        // while this tile's epilogue stages through stage 0
+        int64_t m0n = 0, n0n = 0;
+        bool has_next;
+        {
+            const GemmArgs gt = args();
+            has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
+            if (has_next) {
+                L.P = panels_of<MODE_BS>(gt, m0n, n0n, wave);
+                load_stage<1>(L, 0);
+            }
+        }
+
+        // the last three products of the tile; the next tile's first block
+        // then folds zeros
+#pragma unroll
+        for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
+#pragma unroll
+        for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+        s_tail = 0.f;
+
+        store_tile_halves(acc, args(), m0, n0, wave, lane);
+        if (!has_next) break;
+        wait_dma_and_sync();
+        read_head<1>(a, bf, s, wm, wn, frow, fc);
+#pragma unroll
+        for (int i = 0; i < TM; i++)
+#pragma unroll
+            for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+        vb += (int)gridDim.x;
+        m0 = m0n;
+        n0 = n0n;
     }
 }
 
@@ -765,6 +973,18 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
                    uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                    int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
+    if (g.KB % 2 == 0) {
+        // one workgroup per CU (a multiple of 8, so that the XCD of each
+        // tile is the one the non-persistent launch would give it)
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < NUM_XCD)
+            cus = 256;
+        const int grid = gemm_grid(g), per = cus / NUM_XCD * NUM_XCD;
+        return bs_enqueue(bsgemm_persistent_kernel, dim3(grid < per ? grid : per), dim3(NTHREADS),
+                          stream, g);
+    }
     return bs_enqueue(bsgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
 }
 

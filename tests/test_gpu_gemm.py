@@ -87,6 +87,22 @@ def test_gemm_zero_rows_and_determinism():
     assert np.all(b1[17] == 0) and np.all(b1[300] == 0)
 
 
+@pytest.mark.parametrize("M,bands", [(4252, 4), (4224, 33)])
+def test_gemm_many_tiles_vs_oracle(M, bands):
+    """More tiles than the chip has CUs (17 x 17 = 289), so that workgroups of
+    the persistent kernel (K / 128 even) run two tiles each; element by
+    element against the oracle.  M = 4252: a ragged last M tile and 1063-row
+    bands that begin inside tiles; M = 4224: 33 bands of 128 rows, shorter
+    than a tile."""
+    N, K = 4352, 256
+    qa, sa, qb, sb = operands(M, N, K, seed=7, heavy=True)
+    say(f"bsgemm_fp8 many tiles M={M} N={N} K={K} bands={bands}")
+    _, ref = oracle.bsgemm(qa, sa, qb, sb)
+    _, ref_m = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
+    C = run(qa, sa, qb, sb, bands=bands)
+    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"many tiles M={M} bands={bands}")
+
+
 @pytest.mark.parametrize("M,bands,pad", [(2048, 8, 0), (1024, 4, 136), (20096 // 8, 2, 8)])
 def test_gemm_band_layout(M, bands, pad):
     """Band epilogue: contiguous bands are byte-identical to the row-major
