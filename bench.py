@@ -441,7 +441,7 @@ def main():
                    "M": M, "N": N, "K": K, "P": P, "bands": P},
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / PEAK_FP8_TFLOPS, "traffic": traffic,
-                     "kernel": "bsgemm_tile_kernel", "algorithmic_flop_per_launch": flops},
+                     "kernel": "bsgemm_persistent_kernel", "algorithmic_flop_per_launch": flops},
         "phases": phases,
         "unfused_step": {"ms_per_step": ms_u, "value": flops / (ms_u * 1e-3) / 1e12,
                          "phases_us": {k: v * 1e3 for k, v in phase_u.items()}},
