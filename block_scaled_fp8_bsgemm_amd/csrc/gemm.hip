@@ -37,8 +37,8 @@
 //    panels in that XCD's L2 (its 32 concurrent tiles span 4 M-tiles x 8
 //    N-tiles; measured faster than 8 x 4, 2 x 16 or 1 x 32).
 //
-// When K / 128 is even (the benchmark's K = 2048), the blockscale GEMM runs
-// as a persistent kernel instead: one workgroup per CU walks several tiles,
+// When K / 128 is even (the benchmark's K = 2048), the blockscale and mxfp8
+// GEMMs run as persistent kernels instead: one workgroup per CU walks several tiles,
 // and the next tile's first K block is DMA'd while the finished tile's
 // epilogue runs, so that neither the workgroup launch nor the first block's
 // load latency is paid per tile (bit-identical results).
@@ -781,7 +781,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     for (int r = 0; r < RPW; r++) band_store<MODE>(g, o, r * 8, vrow[r]);
 }
 
-// ---- persistent blockscale kernel (K / 128 even) ----
+// ---- persistent kernels (K / 128 even; blockscale and mxfp8) ----
 // One workgroup per CU walks the tiles of virtual workgroups b, b + G,
 // b + 2G, ... (G = grid size, a multiple of 8, so every tile stays on the XCD
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
@@ -798,6 +798,7 @@ __device__ __forceinline__ uint8_t *pstage_row(int wave, int lr) {
     return (lr < 32 ? sA0 : sB0) + wave * 4096 + (lr & 31) * (WN * 2);
 }
 
+template <int MODE>
 __device__ __forceinline__ void store_tile_halves(const v4f (&acc)[TM][TN], const GemmArgs &g,
                                                   int64_t m0, int64_t n0, int wave, int lane) {
     // opaque to the compiler, so that the addresses below are formed here
@@ -833,11 +834,13 @@ __device__ __forceinline__ void store_tile_halves(const v4f (&acc)[TM][TN], cons
 #pragma unroll
         for (int r = 0; r < RPH; r++) asm volatile("" : "+v"(vrow[r]));
 #pragma unroll
-        for (int r = 0; r < RPH; r++) band_store<MODE_BS>(g, o, h * (WM / 2) + r * 8, vrow[r]);
+        for (int r = 0; r < RPH; r++) band_store<MODE>(g, o, h * (WM / 2) + r * 8, vrow[r]);
     }
 }
 
-__global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g) {
+template <int MODE>
+__device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
+    constexpr bool MX = MODE == MODE_MX;
     int vb = blockIdx.x;
     int64_t m0, n0;
     if (!tile_of(g, vb, m0, n0)) return;
@@ -850,8 +853,8 @@ __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g)
     const int fc = (lane >> 4) * 2;
 
     Loader L;
-    init_loader<MODE_BS>(L, g, wave, lane);
-    L.P = panels_of<MODE_BS>(g, m0, n0, wave);
+    init_loader<MODE>(L, g, wave, lane);
+    L.P = panels_of<MODE>(g, m0, n0, wave);
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -860,11 +863,14 @@ __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g)
         for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
     // block 0 of every tile sits in stage 1 (K / 128 even)
+    const int gq = lane >> 4;   // mxfp8: the lane's 32-wide K group
     v8i a, bf[TN];
     float s[TM];
+    MxScales x;
     load_stage<1>(L, 0);
     wait_dma_and_sync();
-    read_head<1>(a, bf, s, wm, wn, frow, fc);
+    if constexpr (MX) read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
+    else read_head<1>(a, bf, s, wm, wn, frow, fc);
 
     v4f p[4];
 #pragma unroll
@@ -883,8 +889,13 @@ __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g)
     };
     for (;;) {
         for (int kb = 0; kb < KB; kb += 2) {
-            kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
-            kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
+            if constexpr (MX) {
+                kblock_mx<1>(acc, a, bf, x, L, kb, KB, wm, wn, frow, gq);
+                kblock_mx<0>(acc, a, bf, x, L, kb + 1, KB, wm, wn, frow, gq);
+            } else {
+                kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
+                kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
+            }
         }
         // the next tile's block 0 goes to stage 1 (unread after the last
         // block's barrier but for head reads whose values are never used)
@@ -895,23 +906,26 @@ __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g)
             const GemmArgs gt = args();
             has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
             if (has_next) {
-                L.P = panels_of<MODE_BS>(gt, m0n, n0n, wave);
+                L.P = panels_of<MODE>(gt, m0n, n0n, wave);
                 load_stage<1>(L, 0);
             }
         }
 
-        // the last three products of the tile; the next tile's first block
-        // then folds zeros
+        if constexpr (!MX) {
+            // the last three products of the tile; the next tile's first
+            // block then folds zeros
 #pragma unroll
-        for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
+            for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
 #pragma unroll
-        for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
-        s_tail = 0.f;
+            for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
+            s_tail = 0.f;
+        }
 
-        store_tile_halves(acc, args(), m0, n0, wave, lane);
+        store_tile_halves<MODE>(acc, args(), m0, n0, wave, lane);
         if (!has_next) break;
         wait_dma_and_sync();
-        read_head<1>(a, bf, s, wm, wn, frow, fc);
+        if constexpr (MX) read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
+        else read_head<1>(a, bf, s, wm, wn, frow, fc);
 #pragma unroll
         for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -920,6 +934,13 @@ __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g)
         m0 = m0n;
         n0 = n0n;
     }
+}
+
+__global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g) {
+    gemm_persistent<MODE_BS>(g);
+}
+__global__ void __launch_bounds__(NTHREADS) mxgemm_persistent_kernel(GemmArgs g) {
+    gemm_persistent<MODE_MX>(g);
 }
 
 __global__ void __launch_bounds__(NTHREADS) bsgemm_tile_kernel(GemmArgs g) { gemm_tile<MODE_BS>(g); }
@@ -969,22 +990,25 @@ static int gemm_grid(const GemmArgs &g) {
     return ((T + NUM_XCD - 1) / NUM_XCD) * NUM_XCD;
 }
 
+// The persistent kernels' grid: one workgroup per CU, a multiple of 8 so
+// that the XCD of each tile is the one the non-persistent launch gives it.
+static int persistent_grid(const GemmArgs &g) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < NUM_XCD)
+        cus = 256;
+    const int grid = gemm_grid(g), per = cus / NUM_XCD * NUM_XCD;
+    return grid < per ? grid : per;
+}
+
 int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const float *sb,
                    uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                    int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
-    if (g.KB % 2 == 0) {
-        // one workgroup per CU (a multiple of 8, so that the XCD of each
-        // tile is the one the non-persistent launch would give it)
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus < NUM_XCD)
-            cus = 256;
-        const int grid = gemm_grid(g), per = cus / NUM_XCD * NUM_XCD;
-        return bs_enqueue(bsgemm_persistent_kernel, dim3(grid < per ? grid : per), dim3(NTHREADS),
+    if (g.KB % 2 == 0)
+        return bs_enqueue(bsgemm_persistent_kernel, dim3(persistent_grid(g)), dim3(NTHREADS),
                           stream, g);
-    }
     return bs_enqueue(bsgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
 }
 
@@ -1007,5 +1031,8 @@ int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, cons
                      uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                      int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
+    if (g.KB % 2 == 0)
+        return bs_enqueue(mxgemm_persistent_kernel, dim3(persistent_grid(g)), dim3(NTHREADS),
+                          stream, g);
     return bs_enqueue(mxgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);
 }

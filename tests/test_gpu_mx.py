@@ -77,6 +77,19 @@ def test_mxgemm_full_vs_oracle(M, N, K, heavy):
     gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"mx M={M} N={N} K={K}")
 
 
+def test_mxgemm_many_tiles_vs_oracle():
+    """289 tiles, more than the chip has CUs: workgroups of the persistent
+    kernel (K / 128 even) run two tiles each; ragged last M tile and 1063-row
+    bands that begin inside tiles.  Element by element against the oracle."""
+    M, N, K, bands = 4252, 4352, 256, 4
+    say(f"mxgemm_fp8 many tiles M={M} N={N} K={K} bands={bands}")
+    qa, ea, qb, eb = operands(M, N, K, seed=8, heavy=True)
+    _, ref = oracle.mxgemm(qa, ea, qb, eb)
+    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
+    C = run(qa, ea, qb, eb, bands=bands)
+    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"mx many tiles M={M}")
+
+
 def test_mxgemm_unit_scales_exact():
     """Small codes, every scale byte 127: all sums are exact in fp32, so the
     device result equals the oracle bit for bit."""
