@@ -285,9 +285,8 @@ __device__ __forceinline__ void read_head_mx(v8i &a, v8i (&bf)[TN], MxScales &x,
 }
 
 // DMA of block kb + 1 into stage ST ^ 1 during the first nine MFMAs of block
-// kb (see kblock).
-// (The persistent kernel passes the next tile's descriptors and block 0 in
-// the last K block of a tile: dma_block takes them explicitly.)
+// kb (see kblock); dma_block takes the block, its validity and the tile's
+// panels explicitly.
 template <int ST>
 __device__ __forceinline__ void dma_block(const Loader &L, const Panels &P, int k, int kload, bool v) {
     if (k < 9) {
@@ -488,9 +487,8 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             if (i == TM - 1) {
                 bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
             }
-            // the DMA of the next block (kb + 1, or in the persistent kernel's
-            // last block of a tile the next tile's block 0) into the other
-            // stage (unread since the previous block's barrier), one
+            // the DMA of the next block (kload, normally kb + 1) into the
+            // other stage (unread since the previous block's barrier), one
             // instruction after each of the first nine MFMAs, away from the
             // head reads of row group 7
             dma_block<ST>(L, P, k, kload, vload);
