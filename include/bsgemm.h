@@ -219,7 +219,7 @@ bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
  * the GEMM's MFMA consumes them:
  *
  *   Bp[((nt * (K/128) + kb) * 2 + h) * 1024 + (16 g + r) * 16 + e]
- *       = B[16 nt + r, 128 kb + 32 g + 16 h + e]
+ *       = B[16 nt + r, 128 kb + 16 g + 64 h + e]
  *
  * for 16-row group nt, K block kb, half h in {0,1}, g in [0,4), r in [0,16),
  * e in [0,16): each 2 KiB block is one 16 x 128 tile of B, laid out as the

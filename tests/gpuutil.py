@@ -1,5 +1,17 @@
-"""Helpers for the GPU parity tests: device transfer, output poisoning and
-the comparisons used against the oracle."""
+"""Helpers for the GPU parity tests: device transfer, output poisoning, the
+seeded workload operands (cached: several tests use the same full-size
+product), and the GEMM acceptance.
+
+GEMM acceptance rests on the pages' definition, the exact block-scale product
+O4 (O11 for mxfp8): every bf16 output must lie in the interval the
+instruction's truncation and rounding allow around O4's fp32 accumulator
+(oracle/bounds.py derives it; tests/test_oracle_bound.py pins it).  The
+relL2 against O4 is printed for every check; it is above the 3e-5 that the
+pages measure between two implementations sharing the same instruction
+(sglang PR 40757, "Numbers"), because O4 sums each 128-deep block exactly
+and the fp8 MFMA does not.  Agreement with the instruction model O4m is
+printed as a diagnostic; it is asserted only in the conformance test
+(test_gpu_mfma_conformance.py)."""
 import sys
 
 import numpy as np
@@ -7,10 +19,8 @@ import torch
 
 import block_scaled_fp8_bsgemm_amd as bs
 import oracle
-
-# acceptance for bf16 GEMM outputs against the instruction-faithful definition
-# (O4m): what is left is accumulation order only
-GEMM_REL_L2 = 3e-5
+import synth
+from oracle import bounds
 
 
 def device():
@@ -47,21 +57,69 @@ def poison_u8(t):
     return t
 
 
-def gemm_compare(got_bits, ref_mfma_bits, ref_exact_bits, what):
-    """bf16 GEMM output against the oracle's MFMA model (O4m, or O11m for
-    mxfp8; relL2 <= 3e-5) and against its exact definition (O4 / O11: no
-    further than the model itself is from it)."""
-    got = oracle.bf16_to_f64(got_bits)
-    ref_m = oracle.bf16_to_f64(ref_mfma_bits)
-    ref_e = oracle.bf16_to_f64(ref_exact_bits)
-    assert np.all(np.isfinite(got)), f"{what}: non-finite output (unwritten or NaN)"
-    r_m = oracle.rel_l2(got, ref_m)
-    r_e = oracle.rel_l2(got, ref_e)
-    r_me = oracle.rel_l2(ref_m, ref_e)
-    flips_m = int(np.count_nonzero(got_bits != ref_mfma_bits))
-    flips_e = int(np.count_nonzero(got_bits != ref_exact_bits))
-    say(f"{what}: vs MFMA model relL2={r_m:.3e} differing={flips_m}/{got_bits.size}; "
-        f"vs exact relL2={r_e:.3e} differing={flips_e} (model vs exact {r_me:.3e})")
-    assert r_m <= GEMM_REL_L2, (what, "vs MFMA model", r_m)
-    assert r_e <= r_me + GEMM_REL_L2, (what, "vs exact", r_e, r_me)
-    return r_m, flips_m
+_OPERANDS = {}
+_EXACT = {}
+
+
+def workload_operands(M, N, K, seed=0, heavy=True, pad_to=None):
+    """The seeded operands quantized by the oracle's block quantizer (O3),
+    cached per shape: (qa, sa, qb, sb)."""
+    key = (M, N, K, seed, heavy, pad_to)
+    if key not in _OPERANDS:
+        A, B = synth.operand_fp32(M, N, K, seed=seed, heavy=heavy)
+        if pad_to:
+            A = synth.pad_rows(A, pad_to)
+        qa, sa = oracle.quant_blocks(A, 1, 128)
+        qb, sb = oracle.quant_blocks(B, 128, 128)
+        _OPERANDS[key] = (qa, sa, qb, sb)
+    return _OPERANDS[key]
+
+
+def exact_product(qa, sa, qb, sb, key=None):
+    """O4's fp32 accumulator and bf16 output, cached under `key` if given."""
+    if key is not None and key in _EXACT:
+        return _EXACT[key]
+    r = oracle.bsgemm(qa, sa, qb, sb)
+    if key is not None:
+        _EXACT[key] = r
+    return r
+
+
+def _report(what, st, extra=""):
+    say(f"{what}: vs exact relL2={st['rel_l2']:.3e} differing={st['differing']}/{st['elements']}; "
+        f"bound: outside={st['bad']} largest share used={st['worst_used']:.3f}{extra}")
+
+
+def gemm_accept(got_bits, qa, sa, qb, sb, what, key=None, model=True):
+    """Every element of the device's bf16 GEMM output [M, N] against O4 under
+    the derived bound; O4m agreement printed when `model`."""
+    acc, _ = exact_product(qa, sa, qb, sb, key)
+    st = bounds.check_bsgemm(got_bits, acc, qa, sa, qb, sb)
+    extra = ""
+    if model:
+        _, cm = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
+        extra = f"; vs MFMA model differing={int(np.count_nonzero(got_bits != cm))}"
+    _report(what, st, extra)
+    assert st["bad"] == 0, (what, st)
+    return st
+
+
+def gemm_accept_rows(got_bits, rows, qa, sa, qb, sb, what):
+    """Whole output rows `rows` of a product too large for the host
+    (got_bits [len(rows), N]), against O4 on those rows."""
+    qa_r, sa_r = np.ascontiguousarray(qa[rows]), np.ascontiguousarray(sa[rows])
+    return gemm_accept(got_bits, qa_r, sa_r, qb, sb, what, model=False)
+
+
+def mx_accept(got_bits, qa, ea, qb, eb, what, model=True):
+    """The mxfp8 GEMM's bf16 output against O11 under its bound; agreement
+    with the scaled-MFMA model O11m printed when `model`."""
+    acc, _ = oracle.mxgemm(qa, ea, qb, eb)
+    st = bounds.check_mxgemm(got_bits, acc, qa, ea, qb, eb)
+    extra = ""
+    if model:
+        _, cm = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
+        extra = f"; vs MFMA model differing={int(np.count_nonzero(got_bits != cm))}"
+    _report(what, st, extra)
+    assert st["bad"] == 0, (what, st)
+    return st

@@ -1,11 +1,11 @@
-"""GPU parity of bsgemm_fp8 against the oracle (O4 / O4m product, O5 band
-layout).
+"""GPU parity of bsgemm_fp8 against the oracle (O4 product, O5 band layout).
 
 Inputs are the seeded synthetic operands quantized by the oracle's block
-quantizer; both sides consume the same bytes.  Acceptance: relL2 <= 3e-5 on
-the bf16 output against O4m (block dot products as the fp8 MFMA forms them),
-and no further from the exact-block-sum O4 than O4m itself is; bitwise for the
-band layout and for repeated runs."""
+quantizer; both sides consume the same bytes.  Acceptance: every bf16 output
+element inside the interval the fp8 MFMA's truncation and rounding allow
+around the exact product O4 (gpuutil.gemm_accept, oracle/bounds.py), at
+every shape including the benchmark's full sizes; bit for bit where all sums
+are exact; bitwise for the band layout and for repeated runs."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +13,7 @@ import torch
 import block_scaled_fp8_bsgemm_amd as bs
 import oracle
 import synth
-from gpuutil import bits16, device, gemm_compare, poison_bf16, say, to_dev
+from gpuutil import bits16, device, gemm_accept, poison_bf16, say, to_dev, workload_operands
 
 pytestmark = pytest.mark.gpu
 
@@ -51,10 +51,8 @@ def run(qa, sa, qb, sb, bands=1, band_stride=0, C=None):
 def test_gemm_full_vs_oracle(M, N, K, heavy):
     say(f"bsgemm_fp8 M={M} N={N} K={K} heavy={heavy}")
     qa, sa, qb, sb = operands(M, N, K, seed=0, heavy=heavy)
-    _, ref = oracle.bsgemm(qa, sa, qb, sb)
-    _, ref_m = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
     C = run(qa, sa, qb, sb)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"M={M} N={N} K={K}")
+    gemm_accept(bits16(C).reshape(M, N), qa, sa, qb, sb, f"M={M} N={N} K={K}")
 
 
 def test_gemm_unit_scale_exact():
@@ -97,10 +95,8 @@ def test_gemm_many_tiles_vs_oracle(M, bands):
     N, K = 4352, 256
     qa, sa, qb, sb = operands(M, N, K, seed=7, heavy=True)
     say(f"bsgemm_fp8 many tiles M={M} N={N} K={K} bands={bands}")
-    _, ref = oracle.bsgemm(qa, sa, qb, sb)
-    _, ref_m = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
     C = run(qa, sa, qb, sb, bands=bands)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"many tiles M={M} bands={bands}")
+    gemm_accept(bits16(C).reshape(M, N), qa, sa, qb, sb, f"many tiles M={M} bands={bands}")
 
 
 @pytest.mark.parametrize("M,bands,pad", [(2048, 8, 0), (1024, 4, 136), (20096 // 8, 2, 8)])
@@ -125,27 +121,18 @@ def test_gemm_band_layout(M, bands, pad):
 
 
 @pytest.mark.parametrize("M,bands,pad_to", [(4096, 1, None), (16384, 8, None), (20000, 8, 20096)])
-def test_gemm_full_size_sampled(M, bands, pad_to):
+def test_gemm_full_size(M, bands, pad_to):
     """The benchmark shapes (N=7168, K=2048, heavy rows), in the launch
-    configuration the benchmark times, checked on sampled outputs that the
-    oracle computes one by one; padded rows must be exactly zero."""
+    configuration the benchmark times, every output element against the
+    exact product; padded rows must be exactly zero."""
     N, K = synth.HIDDEN, synth.K_SHARD
-    qa, sa, qb, sb = operands(M, N, K, seed=0, heavy=True, pad_to=pad_to)
+    qa, sa, qb, sb = workload_operands(M, N, K, seed=0, heavy=True, pad_to=pad_to)
     Mp = qa.shape[0]
     say(f"bsgemm_fp8 full size M={Mp} bands={bands}")
     C = run(qa, sa, qb, sb, bands=bands)
     out = bits16(C).reshape(Mp, N)  # contiguous bands == row-major
-    mi, ni = synth.sample_indices(Mp, N, 65536, seed=M)
-    # include whole heavy rows and the band boundaries
-    heavy_rows = np.nonzero(np.abs(sa[:, 0]) > 10 * np.median(np.abs(sa[:, 0])))[0][:4]
-    edge_rows = np.array([r for d in range(bands) for r in (d * (Mp // bands), (d + 1) * (Mp // bands) - 1)])
-    extra_m = np.repeat(np.concatenate([heavy_rows, edge_rows]), 64)
-    extra_n = np.tile(np.linspace(0, N - 1, 64).astype(np.int64), len(heavy_rows) + len(edge_rows))
-    mi = np.concatenate([mi, extra_m])
-    ni = np.concatenate([ni, extra_n])
-    _, ref = oracle.bsgemm_elems(qa, sa, qb, sb, mi, ni)
-    _, ref_m = oracle.bsgemm_elems(qa, sa, qb, sb, mi, ni, mfma=True)
-    gemm_compare(out[mi, ni], ref_m, ref, f"M={Mp} sampled")
+    del C
+    gemm_accept(out, qa, sa, qb, sb, f"M={Mp} all elements", key=("wo_b", M, pad_to), model=False)
     if pad_to:
         assert np.all(out[M:] == 0)
 
@@ -167,10 +154,8 @@ def test_gemm_edge_shapes(M, N, K):
     benchmark's depth, even and odd block counts are covered elsewhere)."""
     say(f"bsgemm_fp8 edge M={M} N={N} K={K}")
     qa, sa, qb, sb = operands(M, N, K, seed=5, heavy=True)
-    _, ref = oracle.bsgemm(qa, sa, qb, sb)
-    _, ref_m = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
     C = run(qa, sa, qb, sb)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"edge M={M} N={N} K={K}")
+    gemm_accept(bits16(C).reshape(M, N), qa, sa, qb, sb, f"edge M={M} N={N} K={K}")
     Bp = torch.empty(N * K, dtype=torch.uint8, device=device())
     bs.bprepack_e4m3(to_dev(qb), Bp)
     C2 = poison_bf16(torch.empty(M * N, dtype=torch.bfloat16, device=device()))

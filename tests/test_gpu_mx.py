@@ -1,7 +1,8 @@
 """GPU parity of the mxfp8 variant against the oracle: mxq_e4m3 (O10, the
-32-wide E8M0 operand quantizer) bit for bit, and mxgemm_fp8 against O11m
-(the scaled MFMA's pass arithmetic) at relL2 <= 3e-5, no further from the
-exact O11 than O11m itself is; band layout bitwise.
+32-wide E8M0 operand quantizer) bit for bit, and mxgemm_fp8 against the
+exact mxfp8 product O11, every element inside the interval the scaled
+MFMA's truncation and rounding allow (gpuutil.mx_accept); band layout
+bitwise.
 
 Inputs are the seeded synthetic operands; the GEMM tests quantize them with
 the oracle's O10 so that both sides consume the same bytes, and one test runs
@@ -13,7 +14,7 @@ import torch
 import block_scaled_fp8_bsgemm_amd as bs
 import oracle
 import synth
-from gpuutil import bf16_dev, bits16, device, gemm_compare, poison_bf16, poison_u8, say, to_dev
+from gpuutil import bf16_dev, bits16, device, mx_accept, poison_bf16, poison_u8, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,10 +72,8 @@ def test_mxq_bitexact(rows, cols):
 def test_mxgemm_full_vs_oracle(M, N, K, heavy):
     say(f"mxgemm_fp8 M={M} N={N} K={K} heavy={heavy}")
     qa, ea, qb, eb = operands(M, N, K, seed=1, heavy=heavy)
-    _, ref = oracle.mxgemm(qa, ea, qb, eb)
-    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
     C = run(qa, ea, qb, eb)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"mx M={M} N={N} K={K}")
+    mx_accept(bits16(C).reshape(M, N), qa, ea, qb, eb, f"mx M={M} N={N} K={K}")
 
 
 def test_mxgemm_many_tiles_vs_oracle():
@@ -84,10 +83,8 @@ def test_mxgemm_many_tiles_vs_oracle():
     M, N, K, bands = 4252, 4352, 256, 4
     say(f"mxgemm_fp8 many tiles M={M} N={N} K={K} bands={bands}")
     qa, ea, qb, eb = operands(M, N, K, seed=8, heavy=True)
-    _, ref = oracle.mxgemm(qa, ea, qb, eb)
-    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
     C = run(qa, ea, qb, eb, bands=bands)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, f"mx many tiles M={M}")
+    mx_accept(bits16(C).reshape(M, N), qa, ea, qb, eb, f"mx many tiles M={M}")
 
 
 def test_mxgemm_unit_scales_exact():
@@ -141,7 +138,7 @@ def test_mxgemm_band_layout():
 
 def test_mxq_into_mxgemm():
     """bf16 operands quantized on the device, then multiplied: codes and scales
-    equal O10's, the product matches O11m on them."""
+    equal O10's, the product lies within the bound of O11 on them."""
     M, N, K = 512, 640, 1024
     A, B = synth.operand_fp32(M, N, K, seed=5, heavy=True)
     ab, bb = oracle.bf16_rne_array(A), oracle.bf16_rne_array(B)
@@ -155,22 +152,17 @@ def test_mxq_into_mxgemm():
     torch.cuda.synchronize()
     assert np.array_equal(dqa.cpu().numpy(), qa) and np.array_equal(dea.cpu().numpy(), ea)
     assert np.array_equal(dqb.cpu().numpy(), qb) and np.array_equal(deb.cpu().numpy(), eb)
-    _, ref = oracle.mxgemm(qa, ea, qb, eb)
-    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
-    gemm_compare(bits16(C).reshape(M, N), ref_m, ref, "mxq -> mxgemm")
+    mx_accept(bits16(C).reshape(M, N), qa, ea, qb, eb, "mxq -> mxgemm")
 
 
 @pytest.mark.parametrize("M,N,K,bands", [(16384, 5120, 2048, 1), (4096, 5120, 4096, 8)])
-def test_mxgemm_full_size_sampled(M, N, K, bands):
-    """The mxfp8 wo_b shapes (N = 5120, K = 2048 and 4096), checked on sampled
-    outputs the oracle computes one by one."""
+def test_mxgemm_full_size(M, N, K, bands):
+    """The mxfp8 wo_b shapes (N = 5120, K = 2048 and 4096), every output
+    element against O11."""
     qa, ea, qb, eb = operands(M, N, K, seed=6, heavy=True)
     say(f"mxgemm_fp8 full size M={M} N={N} K={K} bands={bands}")
     out = bits16(run(qa, ea, qb, eb, bands=bands)).reshape(M, N)
-    mi, ni = synth.sample_indices(M, N, 32768, seed=M + K)
-    _, ref = oracle.mxgemm_elems(qa, ea, qb, eb, mi, ni)
-    _, ref_m = oracle.mxgemm_elems(qa, ea, qb, eb, mi, ni, mfma=True)
-    gemm_compare(out[mi, ni], ref_m, ref, f"mx M={M} N={N} K={K} sampled")
+    mx_accept(out, qa, ea, qb, eb, f"mx M={M} N={N} K={K} all elements", model=False)
 
 
 def test_mxgemm_rejects_without_writing():
@@ -187,6 +179,4 @@ def test_mxgemm_rejects_without_writing():
 def test_mxgemm_edge_shapes(M, N, K):
     say(f"mxgemm_fp8 edge M={M} N={N} K={K}")
     qa, ea, qb, eb = operands(M, N, K, seed=7, heavy=True)
-    _, ref = oracle.mxgemm(qa, ea, qb, eb)
-    _, ref_m = oracle.mxgemm(qa, ea, qb, eb, mfma=True)
-    gemm_compare(bits16(run(qa, ea, qb, eb)).reshape(M, N), ref_m, ref, f"mx edge M={M} N={N} K={K}")
+    mx_accept(bits16(run(qa, ea, qb, eb)).reshape(M, N), qa, ea, qb, eb, f"mx edge M={M} N={N} K={K}")

@@ -1,9 +1,9 @@
 """Pins for O12, the prepacked weight layout: a bijection of the N*K bytes
 in which every 2 KiB block is one whole 16-row x 128-column tile of B, the
 blocks ordered by row group then K block, each block's two 1 KiB halves
-splitting every 32-byte lane segment in its first and second 16 bytes, and
-the lanes of a half ordered lane group first (16 K-consecutive rows per
-group).  The device GEMM on prepacked B equalling the plain one bit for bit is
+holding every lane's two 16-byte K chunks (g and g + 4 of the 128-byte K
+segment, g the lane group), and the lanes of a half ordered lane group first
+(16 rows per group).  The device GEMM on prepacked B equalling the plain one bit for bit is
 the remaining check (GPU tests)."""
 import numpy as np
 
@@ -34,9 +34,10 @@ def test_prepack_blocks_are_whole_tiles_in_order():
 
 
 def test_prepack_lane_segments():
-    """Lane l of a block reads, over its two halves, 32 consecutive bytes of one
-    row: row 16 nt + l % 16, columns 32 (l / 16) .. +32 of the K block (the
-    unscaled 16x16x128 MFMA's operand: lane group g holds K [32g, 32g+32))."""
+    """Lane l of a block reads, over its two halves, two 16-byte chunks of one
+    row: row 16 nt + l % 16, columns 16 g .. +16 and 64 + 16 g .. +16 of the K
+    block (g = l / 16): the chunks the GEMM's LDS fragment reads give the same
+    lane, so the MFMA sees the same bytes in the same slots."""
     N, K = 32, 256
     B = ids(N, K)
     out = oracle.bprepack(B).reshape(N // 16, K // 128, 2, 64, 16)
@@ -45,7 +46,8 @@ def test_prepack_lane_segments():
         nt, kb, l = rng.integers(0, N // 16), rng.integers(0, K // 128), rng.integers(0, 64)
         seg = np.concatenate([out[nt, kb, 0, l], out[nt, kb, 1, l]])
         r, g = 16 * nt + l % 16, l // 16
-        assert np.array_equal(seg, B[r, 128 * kb + 32 * g: 128 * kb + 32 * g + 32])
+        k0 = 128 * kb + 16 * g
+        assert np.array_equal(seg, np.concatenate([B[r, k0:k0 + 16], B[r, k0 + 64:k0 + 80]]))
 
 
 def test_prepack_of_uint8_weight():
