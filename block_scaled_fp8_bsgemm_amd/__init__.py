@@ -21,6 +21,10 @@ library has not been built, importing the functions raises immediately.
 Tensors: e4m3 codes are uint8 (or torch.float8_e4m3fn, reinterpreted), bf16
 values are torch.bfloat16 (or int16/uint16 bit patterns), scales float32.
 All tensors must live on the current CUDA (HIP) device and be contiguous.
+The C ABI receives raw pointers and cannot see sizes, so every wrapper checks
+each operand's shape and each output's element count against the sizes the
+call implies before it takes a pointer, and raises ValueError on a mismatch:
+a wrong-shaped buffer never reaches a kernel.
 """
 import ctypes
 import os
@@ -100,6 +104,50 @@ def _ptr(t, dtypes, name):
     return t.data_ptr()
 
 
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _shape(t, shape, name):
+    _need(tuple(t.shape) == tuple(shape), f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _room(t, n, name):
+    _need(t.numel() >= n, f"{name}: {t.numel()} elements, the call writes {n}")
+
+
+def _dims2(t, name):
+    _need(t.dim() == 2, f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape
+
+
+def _band_elems(M, N, bands, band_stride):
+    """elements of C the band epilogue writes (0 when the ABI will reject the
+    band arguments anyway)"""
+    if bands < 1 or M % bands or band_stride < 0:
+        return 0
+    band_rows = M // bands
+    stride = band_stride if band_stride else band_rows * N
+    return (bands - 1) * stride + band_rows * N
+
+
+def _check_gemm_operands(A, a_scale, B, b_scale, kq, what):
+    """A [M,K], B [N,K]; blockscale (kq = 128): a_scale [M,K/128], b_scale
+    [N/128,K/128]; mxfp8 (kq = 32): a_scale [M,K/32], b_scale [N,K/32]."""
+    M, K = _dims2(A, "A")
+    N, K2 = _dims2(B, "B")
+    _need(K2 == K, f"{what}: A is [M,{K}] but B is [N,{K2}]")
+    _need(K % 128 == 0 and N % 128 == 0, f"{what}: K and N must be multiples of 128 (K={K}, N={N})")
+    if kq == 128:
+        _shape(a_scale, (M, K // 128), "a_scale")
+        _shape(b_scale, (N // 128, K // 128), "b_scale")
+    else:
+        _shape(a_scale, (M, K // 32), "a_scale")
+        _shape(b_scale, (N, K // 32), "b_scale")
+    return M, N, K
+
+
 def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -124,12 +172,11 @@ def bsgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0, stream=No
     """C (bf16) = blockscale(A [M,K] e4m3, a_scale [M,K/128]) x blockscale(B [N,K], b_scale [N/128,K/128])^T,
     written as `bands` destination-major row bands (band d at element d*band_stride)."""
     torch = _torch()
-    M, K = A.shape
-    N = B.shape[0]
+    M, N, K = _check_gemm_operands(A, a_scale, B, b_scale, 128, "bsgemm_fp8")
+    need = _band_elems(M, N, bands, band_stride)
     if C is None:
-        band_rows = M // bands if bands > 0 else 0
-        stride = band_stride if band_stride else band_rows * N
-        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+        C = torch.empty(need, dtype=torch.bfloat16, device=A.device)
+    _room(C, need, "C")
     st = load().bsgemm_fp8(_ptr(A, _u8(), "A"), _ptr(a_scale, _f32(), "a_scale"),
                            _ptr(B, _u8(), "B"), _ptr(b_scale, _f32(), "b_scale"),
                            _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
@@ -141,13 +188,14 @@ def band_reduce(parts, out=None, stream=None):
     """out (bf16 [rows,N]) = bf16(sum_p fp32(parts[p])), parts summed in index order."""
     torch = _torch()
     parts = list(parts)
-    rows, N = parts[0].shape
+    _need(len(parts) >= 1, "band_reduce: no parts")
+    rows, N = _dims2(parts[0], "parts[0]")
+    for i, p in enumerate(parts):
+        _shape(p, (rows, N), f"parts[{i}]")
     if out is None:
         out = torch.empty((rows, N), dtype=torch.bfloat16, device=parts[0].device)
+    _room(out, rows * N, "out")
     ptrs = (ctypes.c_void_p * len(parts))(*[_ptr(p, _b16(), "part") for p in parts])
-    for p in parts:
-        if tuple(p.shape) != (rows, N):
-            raise ValueError("all parts must have the same shape")
     st = load().band_reduce(ptrs, len(parts), _ptr(out, _b16(), "out"), rows, N, _stream(stream))
     _check(st, "band_reduce")
     return out
@@ -156,11 +204,13 @@ def band_reduce(parts, out=None, stream=None):
 def rowq_e4m3(x, q=None, scale=None, stream=None):
     """(q uint8 [rows,N], scale fp32 [rows]) = per-row e4m3 quantization of bf16 x."""
     torch = _torch()
-    rows, N = x.shape
+    rows, N = _dims2(x, "x")
     if q is None:
         q = torch.empty((rows, N), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=x.device)
+    _room(q, rows * N, "q")
+    _room(scale, rows, "scale")
     st = load().rowq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                           rows, N, _stream(stream))
     _check(st, "rowq_e4m3")
@@ -170,9 +220,11 @@ def rowq_e4m3(x, q=None, scale=None, stream=None):
 def rowdq_e4m3(q, scale, y=None, stream=None):
     """y (bf16 [rows,N]) = bf16(decode(q) * scale[row])."""
     torch = _torch()
-    rows, N = q.shape
+    rows, N = _dims2(q, "q")
+    _need(scale.numel() == rows, f"scale: {scale.numel()} elements for {rows} rows")
     if y is None:
         y = torch.empty((rows, N), dtype=torch.bfloat16, device=q.device)
+    _room(y, rows * N, "y")
     st = load().rowdq_e4m3(_ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"), _ptr(y, _b16(), "y"),
                            rows, N, _stream(stream))
     _check(st, "rowdq_e4m3")
@@ -182,12 +234,16 @@ def rowdq_e4m3(q, scale, y=None, stream=None):
 def blockq_e4m3(x, block_rows, q=None, scale=None, stream=None):
     """(q uint8 [rows,cols], scale fp32 [ceil(rows/block_rows), cols/128]) for fp32 x."""
     torch = _torch()
-    rows, cols = x.shape
+    rows, cols = _dims2(x, "x")
+    _need(block_rows in (1, 128), f"blockq_e4m3: block_rows must be 1 or 128, got {block_rows}")
+    nscale = ((rows + block_rows - 1) // block_rows) * (cols // 128)
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty(((rows + block_rows - 1) // block_rows, cols // 128), dtype=torch.float32,
                             device=x.device)
+    _room(q, rows * cols, "q")
+    _room(scale, nscale, "scale")
     st = load().blockq_e4m3(_ptr(x, _f32(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                             rows, cols, block_rows, _stream(stream))
     _check(st, "blockq_e4m3")
@@ -197,11 +253,13 @@ def blockq_e4m3(x, block_rows, q=None, scale=None, stream=None):
 def actq_e4m3(x, q=None, scale=None, stream=None):
     """(q uint8 [rows,cols], scale fp32 [rows, cols/128]) = 1x128 e4m3 quantization of bf16 x."""
     torch = _torch()
-    rows, cols = x.shape
+    rows, cols = _dims2(x, "x")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    _room(q, rows * cols, "q")
+    _room(scale, rows * (cols // 128), "scale")
     st = load().actq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                           rows, cols, _stream(stream))
     _check(st, "actq_e4m3")
@@ -212,12 +270,11 @@ def mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0, stream=No
     """C (bf16) = mx(A [M,K] e4m3, a_scale u8 [M,K/32]) x mx(B [N,K] e4m3, b_scale u8 [N,K/32])^T,
     E8M0 scales per 1x32 block, written as `bands` destination-major row bands."""
     torch = _torch()
-    M, K = A.shape
-    N = B.shape[0]
+    M, N, K = _check_gemm_operands(A, a_scale, B, b_scale, 32, "mxgemm_fp8")
+    need = _band_elems(M, N, bands, band_stride)
     if C is None:
-        band_rows = M // bands if bands > 0 else 0
-        stride = band_stride if band_stride else band_rows * N
-        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+        C = torch.empty(need, dtype=torch.bfloat16, device=A.device)
+    _room(C, need, "C")
     st = load().mxgemm_fp8(_ptr(A, _u8(), "A"), _ptr(a_scale, _u8(), "a_scale"),
                            _ptr(B, _u8(), "B"), _ptr(b_scale, _u8(), "b_scale"),
                            _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
@@ -228,11 +285,13 @@ def mxgemm_fp8(A, a_scale, B, b_scale, C=None, bands=1, band_stride=0, stream=No
 def mxq_e4m3(x, q=None, scale=None, stream=None):
     """(q uint8 [rows,cols], scale E8M0 uint8 [rows, cols/32]) = 1x32 mxfp8 quantization of bf16 x."""
     torch = _torch()
-    rows, cols = x.shape
+    rows, cols = _dims2(x, "x")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _room(q, rows * cols, "q")
+    _room(scale, rows * (cols // 32), "scale")
     st = load().mxq_e4m3(_ptr(x, _b16(), "x"), _ptr(q, _u8(), "q"), _ptr(scale, _u8(), "scale"),
                          rows, cols, _stream(stream))
     _check(st, "mxq_e4m3")
@@ -242,9 +301,10 @@ def mxq_e4m3(x, q=None, scale=None, stream=None):
 def bprepack_e4m3(B, Bp=None, stream=None):
     """Bp (uint8, N*K bytes) = the weight B [N,K] e4m3 in bsgemm_fp8_pb's operand order."""
     torch = _torch()
-    N, K = B.shape
+    N, K = _dims2(B, "B")
     if Bp is None:
         Bp = torch.empty(N * K, dtype=torch.uint8, device=B.device)
+    _room(Bp, N * K, "Bp")
     st = load().bprepack_e4m3(_ptr(B, _u8(), "B"), _ptr(Bp, _u8(), "Bp"), N, K, _stream(stream))
     _check(st, "bprepack_e4m3")
     return Bp
@@ -254,14 +314,17 @@ def bsgemm_fp8_pb(A, a_scale, Bp, b_scale, C=None, bands=1, band_stride=0, strea
     """bsgemm_fp8 with the weight prepacked by bprepack_e4m3 (Bp holds N*K bytes; N is
     taken from b_scale, [N/128, K/128])."""
     torch = _torch()
-    M, K = A.shape
+    M, K = _dims2(A, "A")
+    _need(K % 128 == 0, f"bsgemm_fp8_pb: K must be a multiple of 128 (K={K})")
+    _need(b_scale.dim() == 2 and b_scale.shape[1] == K // 128,
+          f"b_scale: shape {tuple(b_scale.shape)}, expected [N/128, {K // 128}]")
     N = b_scale.shape[0] * 128
-    if Bp.numel() != N * K:
-        raise ValueError(f"Bp must hold N*K = {N * K} bytes, got {Bp.numel()}")
+    _shape(a_scale, (M, K // 128), "a_scale")
+    _need(Bp.numel() == N * K, f"Bp must hold N*K = {N * K} bytes, got {Bp.numel()}")
+    need = _band_elems(M, N, bands, band_stride)
     if C is None:
-        band_rows = M // bands if bands > 0 else 0
-        stride = band_stride if band_stride else band_rows * N
-        C = torch.empty(max(0, (bands - 1) * stride + band_rows * N), dtype=torch.bfloat16, device=A.device)
+        C = torch.empty(need, dtype=torch.bfloat16, device=A.device)
+    _room(C, need, "C")
     st = load().bsgemm_fp8_pb(_ptr(A, _u8(), "A"), _ptr(a_scale, _f32(), "a_scale"),
                               _ptr(Bp, _u8(), "Bp"), _ptr(b_scale, _f32(), "b_scale"),
                               _ptr(C, _b16(), "C"), M, N, K, bands, band_stride, _stream(stream))
@@ -273,14 +336,16 @@ def band_rowq_e4m3(parts, q=None, scale=None, stream=None):
     """(q uint8 [rows,N], scale fp32 [rows]) = rowq_e4m3(band_reduce(parts)) in one kernel."""
     torch = _torch()
     parts = list(parts)
-    rows, N = parts[0].shape
-    for p in parts:
-        if tuple(p.shape) != (rows, N):
-            raise ValueError("all parts must have the same shape")
+    _need(len(parts) >= 1, "band_rowq_e4m3: no parts")
+    rows, N = _dims2(parts[0], "parts[0]")
+    for i, p in enumerate(parts):
+        _shape(p, (rows, N), f"parts[{i}]")
     if q is None:
         q = torch.empty((rows, N), dtype=torch.uint8, device=parts[0].device)
     if scale is None:
         scale = torch.empty((rows,), dtype=torch.float32, device=parts[0].device)
+    _room(q, rows * N, "q")
+    _room(scale, rows, "scale")
     ptrs = (ctypes.c_void_p * len(parts))(*[_ptr(p, _b16(), "part") for p in parts])
     st = load().band_rowq_e4m3(ptrs, len(parts), _ptr(q, _u8(), "q"), _ptr(scale, _f32(), "scale"),
                                rows, N, _stream(stream))

@@ -529,21 +529,18 @@ int bs_launch_rowdq(const uint8_t *q, const float *scale, uint16_t *y, int64_t r
 
 int bs_launch_blockq(const float *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,
                      int block_rows, hipStream_t stream) {
-    int rc = 0;
     if (block_rows == 1) {
         const int64_t nblocks = rows * (cols / 128);
         const int64_t threads = nblocks * 16;
         const int64_t wg = (threads + 255) / 256;
         if (wg > 0x7FFFFFFF) return -1;
-        hipLaunchKernelGGL(blockq_1x128_kernel, dim3((unsigned)(wg > 0 ? wg : 1)), dim3(256), 0, stream,
-                           (const u32x4 *)x, (u32x2 *)q, scale, nblocks);
-    } else {
-        const int64_t nb = ((rows + 127) / 128) * (cols / 128);
-        if (nb > 0x7FFFFFFF) return -1;
-        hipLaunchKernelGGL(blockq_128x128_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(256), 0, stream,
-                           x, q, scale, rows, cols);
+        return bs_enqueue(blockq_1x128_kernel, dim3((unsigned)(wg > 0 ? wg : 1)), dim3(256), stream,
+                          (const u32x4 *)x, (u32x2 *)q, scale, nblocks);
     }
-    return rc;
+    const int64_t nb = ((rows + 127) / 128) * (cols / 128);
+    if (nb > 0x7FFFFFFF) return -1;
+    return bs_enqueue(blockq_128x128_kernel, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(256), stream, x, q,
+                      scale, rows, cols);
 }
 
 int bs_launch_actq(const uint16_t *x, uint8_t *q, float *scale, int64_t rows, int64_t cols,

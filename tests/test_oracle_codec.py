@@ -176,3 +176,29 @@ def test_fp8_wire_granularity_table():
             y = t[q] * np.repeat(s.astype(np.float64), w, axis=1)
         r = oracle.rel_l2(y, xf)
         assert abs(r / ref - 1) < 0.005, (w, r, ref)
+
+
+@pytest.mark.parametrize("heavy_rows", [False, True])
+def test_rowq_vs_torch_quotient_cast(heavy_rows):
+    """O7 on full [2048, 7168] rows against an independent formulation in
+    torch: amax per row in fp32, s = amax / 448 (fp32 division), codes =
+    float8_e4m3fn cast of the fp32 quotient x / s clamped to +-448 (torch's
+    cast rounds to nearest even but does not saturate).  A quotient taken as
+    x * (448 / amax), or a scale of 448 / amax, would differ on many codes."""
+    rows, N = 2048, 7168
+    x = synth.wire_rows(rows, N, seed=300)
+    if heavy_rows:
+        # rows spread over many binades, some with tiny or huge amax
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+        mult = np.exp2(np.random.default_rng(5).integers(-60, 60, rows)).astype(np.float32)
+        x = oracle.bf16_rne_array(xf * mult[:, None])
+    q, s = oracle.rowq(x)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    amax = xt.abs().amax(dim=1)
+    st = amax / 448.0
+    qt = (xt / st[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(s.view(np.uint32), st.numpy().view(np.uint32))
+    assert np.array_equal(q, qt)
+    # the multiply-by-reciprocal formulation is not the same function
+    qm = (xt * (448.0 / amax)[:, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.count_nonzero(qm != q) > 0
