@@ -120,6 +120,22 @@ template <int ST> __device__ __forceinline__ float *stS() { return ST ? sS1 : sS
 __device__ __forceinline__ int lds_slot(int r) { return (r & ~15) | ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return lds_slot(r) * 128 + ((c ^ (r & 7)) << 4); }
 
+// B's rows are staged in a permuted order so that the epilogue can store C
+// straight from the accumulators.  Each wave's 64 output columns are four
+// 16-column MFMA sub-tiles j, and the MFMA leaves lane l with 4 consecutive
+// columns 4 (l/16) .. +4 of its sub-tile.  If sub-tile j's fragment row r is
+// B row brow_j(r) = 32 (j/2) + 8 (r/4) + 4 (j%2) + r%4 of the wave's 64, then
+// lane l's columns of sub-tiles 0 and 1 are the 8 consecutive columns
+// 8 (l/16) .. +8 and those of sub-tiles 2 and 3 the 8 at 32 + 8 (l/16): two
+// 16-byte stores per lane and row group.  brow_of(R) applies this to LDS row
+// R = 64 w + 16 j + r of the staged B tile; it is a permutation within each
+// 64-row group, so each wave's columns still lie in one 128-column b_scale
+// block.
+__device__ __forceinline__ int brow_of(int R) {
+    const int j = (R >> 4) & 3, r = R & 15;
+    return (R & ~63) + 32 * (j >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3);
+}
+
 // Every descriptor here is workgroup-uniform; readfirstlane says so to the
 // compiler, which otherwise may keep one in VGPRs and wrap each load through
 // it in a loop over distinct values.
@@ -143,8 +159,10 @@ struct Loader {
     __amdgpu_buffer_rsrc_t rZ;           // zero-size: every load through it reads nothing
     int poff;    // prepacked B: this lane's byte offset in its wave's first fragment
     int pstep;   // prepacked B: bytes from one 16-row group to the next (K/128 * 2 KiB)
-    int voff;    // this lane's byte offset of its chunk in the A / B row panels (even slots i)
+    int voff;    // this lane's byte offset of its chunk in the A row panel (even slots i)
     int voff1;   // the same for odd slots i (the lane's chunk with bit 2 flipped)
+    int voffB;   // the same two for the B panel, whose rows are fetched in the
+    int voffB1;  //   permuted order of brow_of (see there)
     int k4;      // 4 rows of a panel, in bytes
     int soff;    // this lane's byte offset of its scale (a_scale row, or b_scale block)
     int ldsq;    // byte offset of this wave's first 1 KiB LDS slot
@@ -161,14 +179,17 @@ __device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int 
     if (PIECE < 8) {
         const int i = PIECE >> 1;
         const int q = L.ldsq + i * 1024;
-        // slot i's rows are those of slot 0 plus 0, 4, 16, 20 (see load_stage)
-        const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4;
-        if (PIECE & 1)
+        if (PIECE & 1) {
+            // B: slot i's global rows are those of slot 0 plus 0, 8, 4, 12
+            const int vo = ((i & 1) ? L.voffB1 : L.voffB) + (2 * (i & 1) + (i >> 1)) * L.k4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rB : L.rZ, (lds_void *)(stB<ST>() + q),
                                                      16, vo, koff, 0, 0);
-        else
+        } else {
+            // A: slot i's rows are those of slot 0 plus 0, 4, 16, 20 (see load_stage)
+            const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rA : L.rZ, (lds_void *)(stA<ST>() + q),
                                                      16, vo, koff, 0, 0);
+        }
     } else {
         // blockscale: waves 0..3 fetch a_scale of rows 64w..64w+63, waves
         // 4..7 b_scale of the column blocks from the tile's first one on;
@@ -188,7 +209,9 @@ __device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int 
 // 32w + {0, 4, 16, 20}[i] + (l/16) + 8 * ((l/8) % 2) (lds_slot inverted), so
 // every instruction still fetches eight whole 128-byte row segments; the lane
 // fetches logical chunk (l%8) ^ (row & 7) of its row, which realises the
-// swizzle.
+// swizzle.  B's LDS row R holds the tile's B row brow_of(R) (a permutation
+// within each 64-row group), so slot i of wave w fetches B rows 32w + {0, 8,
+// 4, 12}[i] + (l/16) + 16 * ((l/8) % 2).
 template <int ST>
 __device__ __forceinline__ void load_stage(const Loader &L, int kb, bool valid = true) {
     dma_piece<ST, 0>(L, L.P, kb, valid); dma_piece<ST, 1>(L, L.P, kb, valid);
@@ -274,7 +297,11 @@ __device__ __forceinline__ void read_mx_scales(MxScales &x, int wm, int wn, int 
 #pragma unroll
     for (int i = 0; i < TM; i++) x.a[i] = sc[(wm * WM + i * 16 + frow) * 4 + g];
 #pragma unroll
-    for (int j = 0; j < TN; j++) x.b[j] = sc[(BM + wn * WN + j * 16 + frow) * 4 + g];
+    for (int j = 0; j < TN; j++) {
+        // B row brow_of(wn * WN + 16 j + frow): a lane base plus 0, 4, 32, 36
+        const int bro = BM + wn * WN + 8 * (frow >> 2) + (frow & 3) + 32 * (j >> 1) + 4 * (j & 1);
+        x.b[j] = sc[bro * 4 + g];
+    }
 }
 
 template <int ST>
@@ -348,7 +375,8 @@ __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[
 // The prepacked weight holds, for each 16-row group of B and K block, the
 // 2 KiB the MFMA takes as its B operand, in lane order and split in two
 // 1 KiB halves: half h, lane l = 16 g + r: bytes [16 g + 64 h, 16 g + 64 h + 16)
-// of row r's 128-byte K segment.  A wave loads its fragment j of block kb
+// of the 128-byte K segment of the group's fragment row r, which is B row
+// brow_of(16 nt + r) (the order the LDS-staged kernels stage B in).  A wave loads its fragment j of block kb
 // straight into registers with two fully coalesced 1 KiB loads; B needs no
 // LDS and no DMA.  A block past the end loads through the zero-size
 // descriptor.
@@ -502,20 +530,6 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
     a = a_next;
 }
 
-static_assert(2 * WM * WN * 2 == BM * BK, "each operand array holds two waves' bf16 sub-tiles");
-
-// Wave w's private 16 KiB for staging its 128 x 64 bf16 sub-tile: half of
-// one operand array, 128-byte rows, the four 32-byte units of a row rotated
-// by bits 1-2 of the row so that a fragment's 16 rows spread over all banks.
-__device__ __forceinline__ uint8_t *stage_base(int wave) {
-    const int q = wave >> 1;
-    uint8_t *base = q == 0 ? sA0 : q == 1 ? sA1 : q == 2 ? sB0 : sB1;
-    return base + (wave & 1) * (WM * WN * 2);
-}
-__device__ __forceinline__ int stage_off(int lr, int byte) {
-    return lr * (WN * 2) + (byte ^ (((lr >> 1) & 3) << 5));
-}
-
 constexpr int MODE_BS = 0, MODE_PB = 1, MODE_MX = 2;
 
 // Workgroup (or, in the persistent kernel, virtual workgroup) b -> tile,
@@ -577,6 +591,9 @@ __device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wa
     const int chunk = (lane & 7) ^ (lane >> 4);
     L.voff = row * K + chunk * 16;
     L.voff1 = L.voff ^ 64;
+    const int rowB = wave * 32 + (lane >> 4) + 16 * ((lane >> 3) & 1);   // = brow_of(LDS row)
+    L.voffB = rowB * K + chunk * 16;
+    L.voffB1 = L.voffB ^ 64;
     L.k4 = 4 * K;
     L.soff = MODE == MODE_MX ? ((wave & 3) * 64 + lane) * (K / 32)
                              : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
@@ -610,24 +627,109 @@ __device__ __forceinline__ BandOut band_out(const GemmArgs &g, int64_t m0, int64
     o.mlb = o.br - o.r0 < (uint32_t)BM ? (int)(o.br - o.r0) : BM;
     return o;
 }
-// Store one 16-byte piece of tile row ml = o.ml0 + dml (dml a constant).
 template <int MODE>
-__device__ __forceinline__ void band_store(const GemmArgs &g, const BandOut &o, int dml, u32x4 v) {
-    const int ml = o.ml0 + dml;
-    if (ml >= o.rows || !o.col_ok) return;
-    uint16_t *dst;
-    if (o.br >= BM) {
-        dst = g.C + ((ml < o.mlb ? o.off0 : o.off1) + o.lane_off + (int64_t)dml * g.N);
-    } else {
-        const uint32_t rr = o.r0 + (uint32_t)ml;
-        dst = g.C + ((int64_t)(o.d0 + rr / o.br) * g.band_stride + (int64_t)(rr % o.br) * g.N + o.n);
-    }
+__device__ __forceinline__ void store_piece(uint16_t *dst, u32x4 v) {
     // C is written once.  Inside the wo_b step, storing it non-temporally
     // made both the blockscale GEMM and the fused reduce that follows it
     // faster (step 338 -> 331 us); the mxfp8 GEMM, measured on its own,
     // was slower with it (162 -> 167 us) and keeps ordinary stores.
     if constexpr (MODE == MODE_MX) *(u32x4 *)dst = v;
     else __builtin_nontemporal_store(v, (u32x4 *)dst);
+}
+
+// Store one 16-byte piece of tile row ml = o.ml0 + dml (dml a constant) at
+// column o.n + dn.
+template <int MODE>
+__device__ __forceinline__ void band_store(const GemmArgs &g, const BandOut &o, int dml, int dn, u32x4 v) {
+    const int ml = o.ml0 + dml;
+    if (ml >= o.rows || !o.col_ok) return;
+    uint16_t *dst;
+    if (o.br >= BM) {
+        dst = g.C + ((ml < o.mlb ? o.off0 : o.off1) + o.lane_off + (int64_t)dml * g.N + dn);
+    } else {
+        const uint32_t rr = o.r0 + (uint32_t)ml;
+        dst = g.C + ((int64_t)(o.d0 + rr / o.br) * g.band_stride + (int64_t)(rr % o.br) * g.N + o.n + dn);
+    }
+    store_piece<MODE>(dst, v);
+}
+
+// The epilogue: each wave's 128 x 64 bf16 sub-tile goes from the accumulators
+// straight to the destination band, without LDS.  With B's rows staged in the
+// order of brow_of, lane l = r + 16 g (r < 16) holds for row group i the 8
+// consecutive columns 8 g .. +8 ("piece" g of the row's 8 16-byte pieces) of
+// tile row 16 i + r in sub-tiles 0 and 1 (lo), and piece 4 + g in sub-tiles 2
+// and 3 (hi).  Lanes l and l ^ 8 (rows r and r ^ 8) trade their hi pieces
+// with one DPP row rotation by 8; then the lanes with r < 8 hold pieces g and
+// 4 + g of row r and the lanes with r >= 8 pieces 4 + g and g of row r - 8
+// (the X store), and likewise for rows r + 8 (the Y store).  Each store
+// instruction so writes 8 whole 128-byte row segments, which measured faster
+// than 16 half rows.  A wave's columns are either all inside N or all past it
+// (N % 128 == 0).
+__device__ __forceinline__ u32x4 swap_rows8(u32x4 v) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; e++)   // row_ror:8 within each 16-lane row: lane l reads lane l ^ 8
+        r[e] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v[e], 0x128, 0xF, 0xF, false);
+    return r;
+}
+
+// The pieces lane l stores for row group i: x for tile row 16 i + (l % 8) at
+// column piece px, y for tile row 16 i + 8 + (l % 8) at piece px +- 4.
+__device__ __forceinline__ void tile_pieces(const v4f (&acc)[TM][TN], int i, bool up, u32x4 &x, u32x4 &y) {
+    const u32x4 lo = {pack_bf16x2(acc[i][0][0], acc[i][0][1]), pack_bf16x2(acc[i][0][2], acc[i][0][3]),
+                      pack_bf16x2(acc[i][1][0], acc[i][1][1]), pack_bf16x2(acc[i][1][2], acc[i][1][3])};
+    const u32x4 hi = swap_rows8(
+        (u32x4){pack_bf16x2(acc[i][2][0], acc[i][2][1]), pack_bf16x2(acc[i][2][2], acc[i][2][3]),
+                pack_bf16x2(acc[i][3][0], acc[i][3][1]), pack_bf16x2(acc[i][3][2], acc[i][3][3])});
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        x[e] = up ? hi[e] : lo[e];
+        y[e] = up ? lo[e] : hi[e];
+    }
+}
+
+// Whether every row and column of the tile is inside the matrix and the
+// bands are contiguous (C is then plain row-major [M, N]): the epilogue of
+// such a tile takes the fast path of store_tile, and every lane issues all
+// 2 * TM of its stores.
+__device__ __forceinline__ bool tile_is_plain(const GemmArgs &g, int64_t m0, int64_t n0) {
+    return m0 + BM <= g.M && n0 + BN <= g.N && g.band_stride == g.band_rows * g.N;
+}
+
+template <int MODE>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[TM][TN], const GemmArgs &g, int64_t m0,
+                                           int64_t n0, int wave, int lane) {
+    // opaque to the compiler, so that the addresses below are formed here
+    // rather than hoisted out of a tile loop and kept live across it
+    asm volatile("" : "+v"(lane));
+    const int wm = wave >> 2, wn = wave & 3;
+    const bool up = (lane >> 3) & 1;                 // r >= 8
+    const int px = (lane >> 4) + (up ? 4 : 0);       // piece of the X store
+    const int dny = up ? -32 : 32;                   // the Y store's piece, in columns from X's
+    if (tile_is_plain(g, m0, n0)) {
+        // row-major C, no bounds: a uniform base per row group and one
+        // 32-bit lane offset (the tile spans 256 rows of N <= 2^22 elements)
+        const uint32_t lx = (uint32_t)((wm * WM + (lane & 7)) * g.N + wn * WN + px * 8);
+        const uint32_t ly = lx + (uint32_t)(8 * g.N + dny);
+        uint16_t *base = g.C + m0 * g.N + n0;
+#pragma unroll
+        for (int i = 0; i < TM; i++) {
+            u32x4 x, y;
+            tile_pieces(acc, i, up, x, y);
+            uint16_t *bi = base + (int64_t)i * 16 * g.N;
+            store_piece<MODE>(bi + lx, x);
+            store_piece<MODE>(bi + ly, y);
+        }
+        return;
+    }
+    const BandOut o = band_out(g, m0, n0 + wn * WN + px * 8, wm * WM + (lane & 7));
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        u32x4 x, y;
+        tile_pieces(acc, i, up, x, y);
+        band_store<MODE>(g, o, i * 16, 0, x);
+        band_store<MODE>(g, o, i * 16 + 8, dny, y);
+    }
 }
 
 // One 256x256 output tile.  MODE_BS: blockscale operands, A and B staged in
@@ -745,40 +847,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last (empty) DMA is retired
 
-    // ---- epilogue ----
-    // Each wave stages its own 128 x 64 bf16 sub-tile in a private LDS region
-    // and stores it back as 128-byte row segments, eight rows per store
-    // instruction.  No workgroup barrier is needed: after the last K block's
-    // barrier nobody reads the operand stages again (the head reads of the
-    // nonexistent next block fetch values that are never used), and a wave's
-    // own LDS writes are complete once lgkmcnt reaches zero.
-    uint8_t *stg = stage_base(wave);
-#pragma unroll
-    for (int i = 0; i < TM; i++) {
-        const int lr = i * 16 + frow;
-#pragma unroll
-        for (int j = 0; j < TN; j++) {
-            uint2 w;
-            w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-            w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-            *(uint2 *)(stg + stage_off(lr, j * 32 + (lane >> 4) * 8)) = w;
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    // Store r covers sub-tile rows 8r .. 8r+7; lane l the 16 bytes at column
-    // 8 * (l % 8) of row 8r + l / 8.
-    constexpr int RPW = WM / 8;   // store instructions per wave
-    u32x4 vrow[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; r++)
-        vrow[r] = *(const u32x4 *)(stg + stage_off(r * 8 + (lane >> 3), (lane & 7) * 16));
-#pragma unroll
-    for (int r = 0; r < RPW; r++) asm volatile("" : "+v"(vrow[r]));
-
-    const BandOut o = band_out(g, m0, n0 + wn * WN + (lane & 7) * 8, wm * WM + (lane >> 3));
-#pragma unroll
-    for (int r = 0; r < RPW; r++) band_store<MODE>(g, o, r * 8, vrow[r]);
+    store_tile<MODE>(acc, g, m0, n0, wave, lane);
 }
 
 // ---- persistent kernels (K / 128 even; blockscale and mxfp8) ----
@@ -787,57 +856,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
 // one stream.  After a tile's last K block (which always sits in stage 0)
 // the next tile's block 0 is DMA'd into stage 1, unread by then, while the
-// finished tile's epilogue runs, so the first block's load latency and the
-// workgroup launch are hidden behind the epilogue.  That epilogue has only
-// stage 0 to stage through: each wave stages its 128 x 64 bf16 sub-tile in
-// two 64-row halves in the 8 KiB its own DMAs fill (4 KiB of each operand
-// array), which no other wave touches until the next tile's first barrier;
-// no workgroup barrier is needed inside it.  (A variant that issued that DMA
-// from inside the last K block spilled registers in the K loop.)
-__device__ __forceinline__ uint8_t *pstage_row(int wave, int lr) {
-    return (lr < 32 ? sA0 : sB0) + wave * 4096 + (lr & 31) * (WN * 2);
-}
-
-template <int MODE>
-__device__ __forceinline__ void store_tile_halves(const v4f (&acc)[TM][TN], const GemmArgs &g,
-                                                  int64_t m0, int64_t n0, int wave, int lane) {
-    // opaque to the compiler, so that the addresses below are formed here
-    // rather than hoisted out of the tile loop and kept live across it
-    asm volatile("" : "+v"(lane));
-    const int wm = wave >> 2, wn = wave & 3, frow = lane & 15;
-    const BandOut o = band_out(g, m0, n0 + wn * WN + (lane & 7) * 8, wm * WM + (lane >> 3));
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int i = 0; i < TM / 2; i++) {
-            const int lr = i * 16 + frow;
-            uint8_t *row = pstage_row(wave, lr);
-#pragma unroll
-            for (int j = 0; j < TN; j++) {
-                const v4f &c = acc[h * (TM / 2) + i][j];
-                uint2 w;
-                w.x = pack_bf16x2(c[0], c[1]);
-                w.y = pack_bf16x2(c[2], c[3]);
-                *(uint2 *)(row + ((j * 32 + (lane >> 4) * 8) ^ (((lr >> 1) & 3) << 5))) = w;
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's staging writes are done
-        __builtin_amdgcn_wave_barrier();
-        constexpr int RPH = WM / 2 / 8;   // store instructions per half
-        u32x4 vrow[RPH];
-#pragma unroll
-        for (int r = 0; r < RPH; r++) {
-            const int lr = r * 8 + (lane >> 3);
-            vrow[r] = *(const u32x4 *)(pstage_row(wave, lr) + (((lane & 7) * 16) ^ (((lr >> 1) & 3) << 5)));
-        }
-        // the reads are complete before the next half overwrites the region
-#pragma unroll
-        for (int r = 0; r < RPH; r++) asm volatile("" : "+v"(vrow[r]));
-#pragma unroll
-        for (int r = 0; r < RPH; r++) band_store<MODE>(g, o, h * (WM / 2) + r * 8, vrow[r]);
-    }
-}
-
+// finished tile's epilogue stores C from the accumulators, so the first
+// block's load latency and the workgroup launch are hidden behind the
+// epilogue.  (A variant that issued that DMA from inside the last K block
+// spilled registers in the K loop.)
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
     constexpr bool MX = MODE == MODE_MX;
@@ -899,7 +921,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         }
         // the next tile's block 0 goes to stage 1 (unread after the last
         // block's barrier but for head reads whose values are never used)
-        // while this tile's epilogue stages through stage 0
+        // while this tile's epilogue stores
         int64_t m0n = 0, n0n = 0;
         bool has_next;
         {
@@ -921,9 +943,19 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
             s_tail = 0.f;
         }
 
-        store_tile_halves<MODE>(acc, args(), m0, n0, wave, lane);
+        store_tile<MODE>(acc, args(), m0, n0, wave, lane);
         if (!has_next) break;
-        wait_dma_and_sync();
+        // Wait for the next tile's block 0 only: its DMA went out before this
+        // tile's stores, and vector memory operations retire in issue order,
+        // so once no more than the 2 * TM stores of a plain tile are
+        // outstanding, the DMA has landed.  The stores drain under the next
+        // tile's first K block instead.  Other tiles skip stores per lane
+        // and wait for everything.
+        if (tile_is_plain(args(), m0, n0))
+            __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __syncthreads();
         if constexpr (MX) read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
         else read_head<1>(a, bf, s, wm, wn, frow, fc);
 #pragma unroll
@@ -951,8 +983,9 @@ __global__ void __launch_bounds__(NTHREADS) mxgemm_tile_kernel(GemmArgs g) { gem
 
 // B [N, K] -> the prepacked layout [N/16][K/128][2][64][16 B]: unit u of the
 // output (16 bytes) is half h, lane l = 16 g + r of 16-row group nt and K
-// block kb, and holds bytes [16 g + 64 h, +16) of row 16 nt + r's K block kb
-// (the two halves of lane l are the chunks lds_frag gives it).
+// block kb, and holds bytes [16 g + 64 h, +16) of row brow_of(16 nt + r)'s K
+// block kb (the two halves of lane l are the chunks lds_frag gives it; the
+// rows are those the LDS-staged kernel places in the same fragment slot).
 // One lane per output unit: the writes are contiguous, the reads 16-byte
 // aligned gathers.
 __global__ void __launch_bounds__(256)
@@ -964,7 +997,7 @@ bprepack_kernel(const u32x4 *__restrict__ B, u32x4 *__restrict__ Bp, int64_t uni
         const int h = (int)((u >> 6) & 1);
         const int64_t blk = u >> 7;          // nt * KB + kb
         const int64_t nt = blk / KB, kb = blk - nt * KB;
-        const int64_t row = nt * 16 + (l & 15);
+        const int64_t row = (nt & ~(int64_t)3) * 16 + brow_of((int)((nt & 3) * 16 + (l & 15)));
         const int64_t col = kb * 128 + 16 * (l >> 4) + 64 * h;
         Bp[u] = B[(row * K + col) >> 4];
     }

@@ -219,11 +219,13 @@ bs_status actq_e4m3(const uint16_t *x, uint8_t *q, float *scale,
  * the GEMM's MFMA consumes them:
  *
  *   Bp[((nt * (K/128) + kb) * 2 + h) * 1024 + (16 g + r) * 16 + e]
- *       = B[16 nt + r, 128 kb + 16 g + 64 h + e]
+ *       = B[brow(16 nt + r), 128 kb + 16 g + 64 h + e],
+ *   brow(64 b + 16 j + r) = 64 b + 32 (j/2) + 8 (r/4) + 4 (j%2) + r%4
  *
  * for 16-row group nt, K block kb, half h in {0,1}, g in [0,4), r in [0,16),
- * e in [0,16): each 2 KiB block is one 16 x 128 tile of B, laid out as the
- * 64 lanes' operand bytes.  The layout is a contract between this call and
+ * e in [0,16): each 2 KiB block is one 16-row x 128 tile of B, laid out as
+ * the 64 lanes' operand bytes, its rows taken within each 64-row group in the
+ * order the GEMM's epilogue needs (brow).  The layout is a contract between this call and
  * bsgemm_fp8_pb only; nothing infers it from a shape ([PR43480] "Worth a
  * reviewer's attention": one layout read as the other gives garbage, not an
  * error).

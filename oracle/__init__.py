@@ -316,18 +316,29 @@ def mxgemm_elems(qa, ea, qb, eb, mi, ni, mfma=False):
     return acc, c
 
 
+def _brow(R):
+    """the B row a GEMM fragment slot R holds (a permutation within each
+    64-row group): R = 64 b + 16 j + r -> 64 b + 32 (j/2) + 8 (r/4) + 4 (j%2) + r%4"""
+    R = np.asarray(R)
+    j, r = (R >> 4) & 3, R & 15
+    return (R & ~63) + 32 * (j >> 1) + 8 * (r >> 2) + 4 * (j & 1) + (r & 3)
+
+
 def bprepack(B):
     """O12: the weight B [N, K] (any dtype) rearranged into the prepacked
     operand order, flat:  out[((nt*(K/128) + kb)*2 + h)*1024 + (16g + r)*16 + e]
-    = B[16nt + r, 128kb + 16g + 64h + e]  (nt < N/16, kb < K/128, h < 2, g < 4,
-    r < 16, e < 16): each 2 KiB block is one 16 x 128 tile of B in the order
-    the 16x16x128 fp8 MFMA takes its operand, lane l = 16g + r holding K
-    [16g, 16g + 16) of row r in half 0 and K [64 + 16g, 64 + 16g + 16) in
-    half 1.  The gfx950 native mxfp8 route of sglang PR 43480 ("Worth a
+    = B[brow(16nt + r), 128kb + 16g + 64h + e]  (nt < N/16, kb < K/128, h < 2,
+    g < 4, r < 16, e < 16): each 2 KiB block is one 16-row x 128 tile of B in
+    the order the 16x16x128 fp8 MFMA takes its operand, lane l = 16g + r
+    holding K [16g, 16g + 16) of its row in half 0 and K [64 + 16g, +16) in
+    half 1.  The rows of each 64-row group come in the order brow (_brow), the
+    order in which the GEMM places B rows so that its epilogue can store whole
+    16-byte pieces.  The gfx950 native mxfp8 route of sglang PR 43480 ("Worth a
     reviewer's attention") rebinds its weight to the same outer shape
     [N/16, K/128, 2048]."""
     B = np.ascontiguousarray(B)
     N, K = B.shape
-    assert N % 16 == 0 and K % 128 == 0
-    t = B.reshape(N // 16, 16, K // 128, 2, 4, 16)       # nt, r, kb, h, g, e
+    assert N % 64 == 0 and K % 128 == 0
+    Bp = B[_brow(np.arange(N))]
+    t = Bp.reshape(N // 16, 16, K // 128, 2, 4, 16)      # nt, r, kb, h, g, e
     return np.ascontiguousarray(t.transpose(0, 2, 3, 4, 1, 5)).reshape(-1)   # nt, kb, h, g, r, e
