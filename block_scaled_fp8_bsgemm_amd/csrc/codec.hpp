@@ -1,11 +1,12 @@
 // codec.hpp -- bf16 / e4m3 conversions used by the HIP kernels (gfx950).
 //
 // The fp8 format is OCP E4M3 ("fn", max 448), the one gfx950's conversion
-// instructions implement.  Narrowing to e4m3 is: clamp to [-448, 448] in fp32,
-// then v_cvt_pk_fp8_f32, which rounds to nearest even, keeps the sign of zero
-// and handles the subnormal range; narrowing to bf16 is v_cvt_pk_bf16_f32
-// (round to nearest even).  Both instructions were checked against a software
-// round-to-nearest-even encoder on every one of the 2^32 fp32 inputs.
+// instructions implement.  Narrowing to e4m3 is v_cvt_pk_fp8_f32, which rounds
+// to nearest even, keeps the sign of zero and handles the subnormal range (on
+// inputs within +-(448 + 2^-15), see pack_e4m3x4); narrowing to bf16 is
+// v_cvt_pk_bf16_f32 (round to nearest even).  Both instructions were checked
+// against a software round-to-nearest-even encoder on every fp32 input in
+// those ranges.
 //
 // wire_quotient() is shared with a host build: its division is checked on the
 // CPU against IEEE fp32 division for every (x, amax) pair of bf16 values the
@@ -46,13 +47,29 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ inline float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
-
-// four fp32 -> four e4m3 codes in one dword (a in the lowest byte)
+// four fp32 -> four e4m3 codes in one dword (a in the lowest byte), by
+// v_cvt_pk_fp8_f32 (round to nearest even), for inputs of magnitude below 464
+// (the midpoint between 448 and the next e4m3 step, past which the
+// instruction gives NaN).  The quantizers of bf16 data meet only such
+// quotients: with s = RN32(amax / 448) and |x| <= amax, x / s exceeds 448 only
+// by s's rounding, at most one fp32 step while s is normal and at most
+// 448.88 for the subnormal s that the smallest bf16 amax values give (checked
+// for every bf16 amax on the CPU); the E8M0 path scales by an exact power of
+// two chosen so that amax fits 448.  Those values round to the +-448 codes
+// (device test with rows whose amax puts the quotient there).  Dropping the
+// clamp took 1.8 us off the row quantizer's 11.3.
 __device__ inline uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
+}
+
+// The same after clamping to [-448, 448], for the fp32-input block quantizer:
+// an fp32 amax below 448 * 2^-140 gives a subnormal s whose rounding can put
+// x / s far past 464 (a saturating encode maps it to +-448).
+__device__ inline float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+__device__ inline uint32_t pack_e4m3x4_sat(float a, float b, float c, float d) {
+    return pack_e4m3x4(clamp448(a), clamp448(b), clamp448(c), clamp448(d));
 }
 
 #endif

@@ -52,11 +52,29 @@ def rowq_dev(x_bits):
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-@pytest.mark.parametrize("rows,N", [(2048, 7168), (3, 8), (17, 2056), (2, 40960)])
+@pytest.mark.parametrize("rows,N", [(2048, 7168), (3, 8), (17, 2056), (2, 40960),
+                                    (5, 2048), (9, 4096), (6, 8192), (3, 16384), (4, 7160)])
 def test_rowq_bitexact(rows, N):
     say(f"rowq_e4m3 rows={rows} N={N}")
     x = synth.wire_rows(rows, N, seed=200)
     qr, sr = oracle.rowq(x)
+    q, s = rowq_dev(x)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+
+
+@pytest.mark.parametrize("N", [8, 2048, 2056, 4096, 7168, 8192, 16384, 16392])
+def test_rowq_zero_and_negative_zero_rows(N):
+    """All-zero and all -0 rows get scale 0 and +0 codes on every kernel shape
+    (full rows of 64 * CPL packs, guarded rows, long rows)."""
+    say(f"rowq_e4m3 zero rows N={N}")
+    x = synth.wire_rows(6, N, seed=201)
+    x[1] = 0
+    x[3] = 0x8000
+    x[4, ::2] = 0x8000
+    x[4, 1::2] = 0
+    qr, sr = oracle.rowq(x)
+    assert sr[1] == 0 and sr[3] == 0 and sr[4] == 0 and not np.any(qr[[1, 3, 4]])
     q, s = rowq_dev(x)
     assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
     assert np.array_equal(q, qr)
@@ -94,6 +112,50 @@ def test_rowq_exhaustive_bf16():
     assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
     bad = np.argwhere(q != qr)
     assert bad.size == 0, [(int(r), int(c), hex(x[r, c]), hex(q[r, c]), hex(qr[r, c])) for r, c in bad[:8]]
+
+
+def overflow_edge_rows(cols=128):
+    """One row per bf16 amax whose largest quotient x / s lands above 448
+    (3217 of them: s = fl32(amax / 448) rounded down; up to 448.88 where s is
+    subnormal): +-amax at both ends of the row, random smaller values between.
+    The quantizers convert these quotients without a clamp."""
+    b = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = (b << 16).view(np.float32)
+    q = (amax.astype(np.float64) * (1.0 / (amax / np.float32(448.0)).astype(np.float64))).astype(np.float32)
+    over = b[q > 448.0].astype(np.uint16)
+    rng = np.random.default_rng(17)
+    frac = rng.random((over.size, cols)).astype(np.float32)
+    mag = (over.astype(np.uint32) << 16).view(np.float32)
+    rows = oracle.bf16_rne_array(frac * mag[:, None])
+    rows = np.minimum(rows & 0x7FFF, over[:, None]) | (rows & 0x8000)
+    rows[:, 0] = over
+    rows[:, -1] = over | 0x8000
+    return rows.astype(np.uint16)
+
+
+@pytest.mark.parametrize("cols", [128, 2048])
+def test_quantizers_at_the_e4m3_edge(cols):
+    """Rows whose largest quotient exceeds 448 by the rounding of the scale:
+    the row, activation (1x128) and fused reduce + row quantizers give the
+    oracle's (saturating) codes, +-448 at the extremes, with no NaN code."""
+    x = overflow_edge_rows(cols)
+    say(f"quantizers at the e4m3 edge {x.shape}")
+    qr, sr = oracle.rowq(x)
+    assert np.all(qr[:, 0] == 0x7E) and np.all(qr[:, -1] == 0xFE)
+    q, s = rowq_dev(x)
+    assert np.array_equal(s.view(np.uint32), sr.view(np.uint32))
+    assert np.array_equal(q, qr)
+    x32 = (x.astype(np.uint32) << 16).view(np.float32)
+    qa_r, sa_r = oracle.quant_blocks(x32, 1, 128)
+    qa, sa = bs.actq_e4m3(bf16_dev(x))
+    qf = poison_u8(torch.empty(x.shape, dtype=torch.uint8, device=device()))
+    sf = torch.full((x.shape[0],), float("nan"), dtype=torch.float32, device=device())
+    bs.band_rowq_e4m3([bf16_dev(x)], qf, sf)
+    torch.cuda.synchronize()
+    assert np.array_equal(qa.cpu().numpy(), qa_r)
+    assert np.array_equal(sa.cpu().numpy().view(np.uint32), sa_r.view(np.uint32))
+    assert np.array_equal(qf.cpu().numpy(), qr)
+    assert np.array_equal(sf.cpu().numpy().view(np.uint32), sr.view(np.uint32))
 
 
 @pytest.mark.parametrize("rows,N", [(16384, 7168), (7, 24), (3, 33000)])

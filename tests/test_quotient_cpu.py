@@ -52,3 +52,23 @@ def test_wire_quotient_equals_ieee_division(tmp_path):
     pairs, bad = map(int, out.split())
     assert pairs > 1_000_000_000
     assert bad == 0
+
+
+def test_bf16_quotients_stay_below_the_e4m3_overflow_midpoint():
+    """The quantizers of bf16 data convert quotients without clamping them:
+    for every finite nonzero bf16 amax and s = fl32(amax / 448), the largest
+    quotient the kernels form, wire_quotient(amax, 1 / s), stays below 464
+    (the midpoint between 448 and the next e4m3 step).  It exceeds 448 only by
+    the rounding of s: one fp32 step (448 + 2^-15) while s is normal, up to
+    448.88 where s is subnormal.  Those amax values are the ones the device
+    test feeds the row quantizer (test_gpu_stream.py)."""
+    import numpy as np
+    b = np.arange(1, 0x7F80, dtype=np.uint32)
+    amax = (b << 16).view(np.float32)
+    s = amax / np.float32(448.0)
+    assert np.all(s > 0)
+    q = (amax.astype(np.float64) * (1.0 / s.astype(np.float64))).astype(np.float32)
+    assert q.max() < 464.0 and q.max() < 449.0, q.max()
+    normal = s >= np.float32(2.0 ** -126)
+    assert q[normal].max() == np.float32(448.0 + 2.0 ** -15)
+    assert np.count_nonzero(q > 448.0) > 1000
