@@ -27,10 +27,10 @@
 //  - the K block's a_scale values of the tile's 256 rows and its b_scale
 //    values are DMA'd into LDS with the operands; each wave forms its rows'
 //    combined scales a_scale * b_scale in registers;
-//  - at the end each wave stages its 128 x 64 bf16 sub-tile in LDS of its
-//    own and stores it as whole 128-byte row segments of the destination
-//    band, eight rows per instruction, with no workgroup barrier
-//    (non-temporal stores in the blockscale kernels);
+//  - at the end each wave stores its 128 x 64 bf16 sub-tile straight from
+//    the accumulators as whole 128-byte row segments of the destination
+//    band, eight rows per instruction (B's rows are staged in an order that
+//    makes this possible; non-temporal stores in the blockscale kernels);
 //  - workgroup -> tile mapping is XCD-aware: workgroups are dealt to the 8
 //    XCDs round-robin, so each XCD is given a contiguous run of tiles, ordered
 //    in groups of 4 M-tiles so that concurrently running tiles share A and B
@@ -38,10 +38,10 @@
 //    N-tiles; measured faster than 8 x 4, 2 x 16 or 1 x 32).
 //
 // When K / 128 is even (the benchmark's K = 2048), the blockscale and mxfp8
-// GEMMs run as persistent kernels instead: one workgroup per CU walks several tiles,
-// and the next tile's first K block is DMA'd while the finished tile's
-// epilogue runs, so that neither the workgroup launch nor the first block's
-// load latency is paid per tile (bit-identical results).
+// GEMMs run as persistent kernels instead: one workgroup per CU walks several
+// tiles, so the workgroup launch is not paid per tile.  In the blockscale one
+// a finished tile's stores go out inside the next tile's first K block,
+// between its MFMAs (bit-identical results).
 //
 // A second blockscale kernel reads B in a prepacked form (the same bytes in the
 // MFMA's operand order, written once by bprepack_kernel) straight into
@@ -239,6 +239,19 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t *st, int r, int g) {
 __device__ __forceinline__ void fold4(v4f &acc, const v4f &p, float s) {
 #pragma unroll
     for (int e = 0; e < 4; e++) acc[e] = __builtin_fmaf(p[e], s, acc[e]);
+}
+
+// A workgroup barrier that leaves vector memory operations in flight:
+// __syncthreads() also fences global memory, which makes the compiler wait
+// for every outstanding store before it.  The caller waits for what the
+// barrier must cover (its DMA) with its own s_waitcnt; the LDS reads issued
+// before are waited for here, and the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_lds_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void wait_dma_and_sync() {
@@ -850,16 +863,93 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     store_tile<MODE>(acc, g, m0, n0, wave, lane);
 }
 
+// The first K block of every tile in the persistent blockscale kernel.  It
+// carries no products over from a previous block, and the first fold of each
+// sub-tile, three MFMAs after its MFMA as in kblock, sets the accumulator to
+// fma(p, s, +0), which is what folding into a zeroed accumulator gives; the
+// last three sub-tiles, whose first fold is the next block's, are zeroed
+// once stored.  So the accumulators may still hold the previous tile when the
+// block starts:
+// if that tile was a plain one (see tile_is_plain), its epilogue goes out
+// here, the stores of its row group i just before MFMA 4 i, the last reads
+// of those accumulators.  The C stores so drain while the MFMAs of the new
+// tile run, not between tiles.  rC is a descriptor of the previous tile's
+// part of C from its first element on (row-major C: contiguous bands), or
+// the zero-size one when there is nothing to store: the stores are always
+// issued, so that every wave runs the same instructions and the vector
+// memory count below is exact.  lx and ly are the lane's two store offsets
+// in a row group and up its half (see store_tile), in elements.  The DMA of
+// block 1 goes out after MFMAs 0..8 as in kblock, before the stores of row
+// groups 3..6, so at the barrier before row group 7 this wave's DMA has
+// landed once at most those 8 stores are outstanding (vector memory
+// operations retire in issue order).
+template <int ST>
+__device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
+                                             v8i (&bf)[TN], float (&s)[TM], const Loader &L,
+                                             const Panels &P, int kload, bool vload, int wm, int wn,
+                                             int frow, int fc, __amdgpu_buffer_rsrc_t rC,
+                                             int64_t N, uint32_t lx, uint32_t ly, bool up) {
+    const uint8_t *as = stA<ST>();
+    v8i an = a;
+    v8i a_next = a;
+    RawScales rn;
+#pragma unroll
+    for (int i = 0; i < TM; i++) {
+        const v8i af = an;
+        if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
+        if (i == TM - 1) {
+            __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): the stores of row groups 3..6 may remain
+            barrier_lds_only();
+            a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
+            read_scales<ST ^ 1>(rn, wm, wn, frow);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; j++) {
+            const int k = i * TN + j;
+            if (j == 0) {
+                u32x4 x, y;
+                tile_pieces(acc, i, up, x, y);
+                const uint32_t ri = (uint32_t)(i * 16 * N);   // the row group's first element
+                __builtin_amdgcn_raw_buffer_store_b128(x, rC, 2 * (ri + lx), 0, 2);   // 2: nt
+                __builtin_amdgcn_raw_buffer_store_b128(y, rC, 2 * (ri + ly), 0, 2);
+                if (i == TM - 1) {
+                    // products 29..31 are first folded by the next block, which
+                    // adds them (fma into the accumulator): start those at zero
+#pragma unroll
+                    for (int jj = 1; jj < TN; jj++) acc[i][jj] = (v4f){0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            p[k & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                bf[j], af, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+            if (k >= 3) {
+                const int kp = k - 3;
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    acc[kp / TN][kp % TN][e] = __builtin_fmaf(p[kp & 3][e], s[kp / TN], 0.0f);
+            }
+            if (i == TM - 1) {
+                bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, fc);
+            }
+            dma_block<ST>(L, P, k, kload, vload);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    s_tail = s[TM - 1];
+    combine_scales(s, rn);
+    a = a_next;
+}
+
 // ---- persistent kernels (K / 128 even; blockscale and mxfp8) ----
 // One workgroup per CU walks the tiles of virtual workgroups b, b + G,
 // b + 2G, ... (G = grid size, a multiple of 8, so every tile stays on the XCD
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
 // one stream.  After a tile's last K block (which always sits in stage 0)
-// the next tile's block 0 is DMA'd into stage 1, unread by then, while the
-// finished tile's epilogue stores C from the accumulators, so the first
-// block's load latency and the workgroup launch are hidden behind the
-// epilogue.  (A variant that issued that DMA from inside the last K block
-// spilled registers in the K loop.)
+// the next tile's block 0 is DMA'd into stage 1, unread by then.  Blockscale:
+// a plain tile's epilogue then goes out inside the next tile's first K block
+// (kblock_first), between its MFMAs; the last tile and tiles that are not
+// plain store at once.  mxfp8: the epilogue stores C from the accumulators
+// while that DMA is in flight.  (A variant that issued the DMA from inside
+// the last K block spilled registers in the K loop.)
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
     constexpr bool MX = MODE == MODE_MX;
@@ -909,12 +999,33 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         asm volatile("" : "+s"(q));
         return *(const GemmArgs *)q;
     };
+    // blockscale: whether the accumulators hold the previous tile, whose
+    // stores then go out inside this tile's first K block (kblock_first), and
+    // that tile's origin
+    bool pend = false;
+    int64_t pm0 = 0, pn0 = 0;
     for (;;) {
-        for (int kb = 0; kb < KB; kb += 2) {
-            if constexpr (MX) {
+        if constexpr (MX) {
+            for (int kb = 0; kb < KB; kb += 2) {
                 kblock_mx<1>(acc, a, bf, x, L, kb, KB, wm, wn, frow, gq);
                 kblock_mx<0>(acc, a, bf, x, L, kb + 1, KB, wm, wn, frow, gq);
-            } else {
+            }
+        } else {
+            {
+                const GemmArgs gt = args();
+                int ln = lane;
+                asm volatile("" : "+v"(ln));   // form the store offsets here, per tile
+                const bool up = (ln >> 3) & 1;
+                const int px = (ln >> 4) + (up ? 4 : 0);
+                const uint32_t lx = (uint32_t)((wm * WM + (ln & 7)) * gt.N + wn * WN + px * 8);
+                const uint32_t ly = lx + (uint32_t)(8 * gt.N + (up ? -32 : 32));
+                const __amdgpu_buffer_rsrc_t rC =
+                    pend ? make_rsrc(gt.C + pm0 * gt.N + pn0, (gt.M - pm0) * gt.N * 2) : L.rZ;
+                kblock_first<1>(acc, p, s_tail, a, bf, s, L, L.P, 1, true, wm, wn, frow, fc, rC,
+                                gt.N, lx, ly, up);
+            }
+            kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, 2, 2 < KB, wm, wn, frow, fc);
+            for (int kb = 2; kb < KB; kb += 2) {
                 kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
                 kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
             }
@@ -934,34 +1045,43 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         }
 
         if constexpr (!MX) {
-            // the last three products of the tile; the next tile's first
-            // block then folds zeros
+            // the last three products of the tile (kblock_first carries none)
 #pragma unroll
             for (int j = 1; j < TN; j++) fold4(acc[TM - 1][j], p[(TM * TN - TN + j) & 3], s_tail);
-#pragma unroll
-            for (int q = 0; q < 4; q++) p[q] = (v4f){0.f, 0.f, 0.f, 0.f};
-            s_tail = 0.f;
         }
 
-        store_tile<MODE>(acc, args(), m0, n0, wave, lane);
-        if (!has_next) break;
-        // Wait for the next tile's block 0 only: its DMA went out before this
-        // tile's stores, and vector memory operations retire in issue order,
-        // so once no more than the 2 * TM stores of a plain tile are
-        // outstanding, the DMA has landed.  The stores drain under the next
-        // tile's first K block instead.  Other tiles skip stores per lane
-        // and wait for everything.
-        if (tile_is_plain(args(), m0, n0))
-            __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        __syncthreads();
-        if constexpr (MX) read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
-        else read_head<1>(a, bf, s, wm, wn, frow, fc);
+        if constexpr (MX) {
+            store_tile<MODE>(acc, args(), m0, n0, wave, lane);
+            if (!has_next) break;
+            // Wait for the next tile's block 0 only: its DMA went out before
+            // this tile's stores, and vector memory operations retire in
+            // issue order, so once no more than the 2 * TM stores of a plain
+            // tile are outstanding, the DMA has landed.  The stores drain
+            // under the next tile's first K block instead.  Other tiles skip
+            // stores per lane and wait for everything.
+            if (tile_is_plain(args(), m0, n0))
+                __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            __syncthreads();
+            read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
 #pragma unroll
-        for (int i = 0; i < TM; i++)
+            for (int i = 0; i < TM; i++)
 #pragma unroll
-            for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+        } else {
+            // A plain tile's stores go out inside the next tile's first K
+            // block; the last tile and other tiles store here.
+            const bool plain = tile_is_plain(args(), m0, n0);
+            if (!has_next || !plain) store_tile<MODE>(acc, args(), m0, n0, wave, lane);
+            if (!has_next) break;
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile's block 0 has landed
+            __syncthreads();
+            read_head<1>(a, bf, s, wm, wn, frow, fc);
+            pend = plain;
+            pm0 = m0;
+            pn0 = n0;
+        }
         vb += (int)gridDim.x;
         m0 = m0n;
         n0 = n0n;
