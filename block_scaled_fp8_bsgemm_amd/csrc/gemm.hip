@@ -299,21 +299,55 @@ __device__ __forceinline__ void read_head(v8i &a, v8i (&bf)[TN], float (&s)[TM],
 // values [16g, 16g+16) and [64+16g, 64+16g+16) of row l%16 (g = l/16), the
 // placement lds_frag gives, and lane l's scale byte as the E8M0 scale of that
 // row's 32-wide block g: byte g of the row's 4 scale bytes for the K block.
+// The scale bytes are held four to a register: byte i % 4 of a[i / 4] for A
+// row group i, byte j of b for B column group j.  The scaled MFMA's op_sel
+// picks the byte (mx_mfma), so a wave holds 3 registers of scales, not 12.
 struct MxScales {
-    int a[TM];   // A rows of the wave's 8 row groups
-    int b[TN];   // B rows of its 4 column groups
+    int a[TM / 4];   // A rows of the wave's 8 row groups
+    int b;           // B rows of its 4 column groups
 };
+
+__device__ __forceinline__ int pack4(int b0, int b1, int b2, int b3) {
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
 
 template <int ST>
 __device__ __forceinline__ void read_mx_scales(MxScales &x, int wm, int wn, int frow, int g) {
     const uint8_t *sc = (const uint8_t *)stS<ST>();
+    int v[TM];
 #pragma unroll
-    for (int i = 0; i < TM; i++) x.a[i] = sc[(wm * WM + i * 16 + frow) * 4 + g];
+    for (int i = 0; i < TM; i++) v[i] = sc[(wm * WM + i * 16 + frow) * 4 + g];
+    x.a[0] = pack4(v[0], v[1], v[2], v[3]);
+    x.a[1] = pack4(v[4], v[5], v[6], v[7]);
+    int w[TN];
 #pragma unroll
     for (int j = 0; j < TN; j++) {
         // B row brow_of(wn * WN + 16 j + frow): a lane base plus 0, 4, 32, 36
         const int bro = BM + wn * WN + 8 * (frow >> 2) + (frow & 3) + 32 * (j >> 1) + 4 * (j & 1);
-        x.b[j] = sc[bro * 4 + g];
+        w[j] = sc[bro * 4 + g];
+    }
+    x.b = pack4(w[0], w[1], w[2], w[3]);
+}
+
+// The scaled MFMA of A row group i and B column group j (both compile-time
+// after unrolling), each scale byte selected by op_sel.
+template <int OB>
+__device__ __forceinline__ v4f mx_mfma_j(const v8i &b, const v8i &a, const v4f &c, int sb, int sa, int i) {
+    switch (i & 3) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, OB, sb, 0, sa);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, OB, sb, 1, sa);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, OB, sb, 2, sa);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, OB, sb, 3, sa);
+    }
+}
+__device__ __forceinline__ v4f mx_mfma(const v8i &b, const v8i &a, const v4f &c, const MxScales &x, int i,
+                                       int j) {
+    const int sa = x.a[i >> 2];
+    switch (j) {
+    case 0: return mx_mfma_j<0>(b, a, c, x.b, sa, i);
+    case 1: return mx_mfma_j<1>(b, a, c, x.b, sa, i);
+    case 2: return mx_mfma_j<2>(b, a, c, x.b, sa, i);
+    default: return mx_mfma_j<3>(b, a, c, x.b, sa, i);
     }
 }
 
@@ -373,8 +407,7 @@ __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int k = i * TN + j;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                bf[j], af, acc[i][j], 0, 0, 0, x.b[j], 0, x.a[i]);
+            acc[i][j] = mx_mfma(bf[j], af, acc[i][j], x, i, j);
             if (i == TM - 1) bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, g);
             dma_next<ST>(L, k, kb, KB);
             __builtin_amdgcn_sched_barrier(0);
