@@ -489,7 +489,9 @@ def cpu_baseline(ops, c_dev, M, N, K, P, target_s=10.0):
     st = bounds.check_bsgemm(c_dev[:R], acc, qa[:R], sa[:R], qb, sb)
     say(f"validated {R} rows in {time.perf_counter() - t0:.1f} s: {st}")
     val = {"ok": st["bad"] == 0, "rows": R, "elements": st["elements"], "outside_bound": st["bad"],
-           "rel_l2_vs_exact": st["rel_l2"], "bf16_differing_from_exact": st["differing"],
+           "rel_l2_vs_exact": st["rel_l2"], "rel_l2_heaviest_1pct_rows": st["rel_l2_heavy"],
+           "rel_l2_other_rows": st["rel_l2_rest"], "rel_l2_worst_row": st["rel_l2_row_max"],
+           "bf16_differing_from_exact": st["differing"],
            "check": "every element of the last timed step's C on these rows inside the interval the fp8 "
                     "MFMA's truncation and rounding allow around the oracle's exact product"}
     return base, val

@@ -177,8 +177,10 @@ def _check_rows(got_bits, acc_ref, bound, r0, r1):
     worst = float(np.max(used[ok])) if ok.any() else 0.0
     got = bf16_bits_to_f64(got_bits[r0:r1])
     ref = bf16_rne_f64(np.asarray(acc_ref[r0:r1], np.float64))
-    return (nb, first_bad, worst, int(np.count_nonzero(got != ref)), float(np.sum((got - ref) ** 2)),
-            float(np.sum(ref * ref)))
+    row_num = np.sum((got - ref) ** 2, axis=1)
+    row_den = np.sum(ref * ref, axis=1)
+    return (nb, first_bad, worst, int(np.count_nonzero(got != ref)), float(np.sum(row_num)),
+            float(np.sum(row_den)), row_num, row_den)
 
 
 def check_gemm(got_bits, acc_ref, bound, chunk=512, workers=None):
@@ -188,7 +190,10 @@ def check_gemm(got_bits, acc_ref, bound, chunk=512, workers=None):
     (numpy releases the GIL).  Returns a dict: bad (elements outside their
     interval), first_bad, worst_used (largest share of a half-interval used),
     differing (bf16 codes other than rne(acc_ref)), rel_l2 against
-    rne(acc_ref)."""
+    rne(acc_ref); and, since a few large rows can dominate the norm, per-row
+    figures: rel_l2_row_max (the worst row's relL2), rel_l2_heavy over the 1 %
+    of rows with the largest reference norm (at least one row) and
+    rel_l2_rest over the others.  These are reports, not acceptance."""
     import concurrent.futures as cf
     import os
     M, N = got_bits.shape
@@ -198,11 +203,23 @@ def check_gemm(got_bits, acc_ref, bound, chunk=512, workers=None):
     with cf.ThreadPoolExecutor(workers) as ex:
         res = list(ex.map(lambda s: _check_rows(got_bits, acc_ref, bound, *s), spans))
     num, den = sum(r[4] for r in res), sum(r[5] for r in res)
-    rel = float(np.sqrt(num) / np.sqrt(den)) if den > 0 else float(np.sqrt(num))
+
+    def rel_of(n, d):
+        return float(np.sqrt(n) / np.sqrt(d)) if d > 0 else float(np.sqrt(n))
+
+    row_num = np.concatenate([r[6] for r in res]) if res else np.zeros(0)
+    row_den = np.concatenate([r[7] for r in res]) if res else np.zeros(0)
+    nz = row_den > 0
+    row_max = float(np.max(np.sqrt(row_num[nz] / row_den[nz]))) if nz.any() else 0.0
+    heavy = np.zeros(M, bool)
+    if M:
+        heavy[np.argsort(row_den)[::-1][: max(1, M // 100)]] = True
     return {"elements": M * N, "bad": sum(r[0] for r in res),
             "first_bad": next((r[1] for r in res if r[1] is not None), None),
             "worst_used": max([r[2] for r in res] + [0.0]), "differing": sum(r[3] for r in res),
-            "rel_l2": rel}
+            "rel_l2": rel_of(num, den), "rel_l2_row_max": row_max,
+            "rel_l2_heavy": rel_of(float(np.sum(row_num[heavy])), float(np.sum(row_den[heavy]))),
+            "rel_l2_rest": rel_of(float(np.sum(row_num[~heavy])), float(np.sum(row_den[~heavy])))}
 
 
 def check_bsgemm(got_bits, acc_ref, qa, sa, qb, sb, **kw):

@@ -86,7 +86,9 @@ def exact_product(qa, sa, qb, sb, key=None):
 
 
 def _report(what, st, extra=""):
-    say(f"{what}: vs exact relL2={st['rel_l2']:.3e} differing={st['differing']}/{st['elements']}; "
+    say(f"{what}: vs exact relL2={st['rel_l2']:.3e} (heaviest 1% of rows {st['rel_l2_heavy']:.3e}, "
+        f"other rows {st['rel_l2_rest']:.3e}, worst row {st['rel_l2_row_max']:.3e}) "
+        f"differing={st['differing']}/{st['elements']}; "
         f"bound: outside={st['bad']} largest share used={st['worst_used']:.3f}{extra}")
 
 

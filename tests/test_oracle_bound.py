@@ -160,3 +160,23 @@ def test_mx_planted_mistakes_fall_outside(name):
     _, cm = oracle.mxgemm(qa2, ea2, qb2, eb, mfma=True)
     st = bounds.check_mxgemm(cm, acc, qa, ea, qb, eb)
     assert st["bad"] > 0, (name, st)
+
+
+def test_row_figures_expose_an_error_that_the_norm_hides():
+    """relL2 over the whole output is dominated by the few x50 rows; an error
+    confined to one ordinary row shows in the worst-row and other-rows
+    figures while the global figure barely moves."""
+    qa, sa, qb, sb = quantized(512, 256, 256, seed=4, heavy=True)
+    acc, _ = oracle.bsgemm(qa, sa, qb, sb)
+    _, cm = oracle.bsgemm(qa, sa, qb, sb, mfma=True)
+    clean = check(cm, acc, (qa, sa, qb, sb))
+    norms = np.sum(acc.astype(np.float64) ** 2, axis=1)
+    r = int(np.argsort(norms)[len(norms) // 2])      # an ordinary row
+    bad = cm.copy()
+    bad[r] ^= 0x0040                                  # one bf16 mantissa bit flipped across the row
+    st = check(bad, acc, (qa, sa, qb, sb))
+    assert st["bad"] > 0
+    assert st["rel_l2_row_max"] > 50 * clean["rel_l2_row_max"] or st["rel_l2_row_max"] > 1e-2
+    assert st["rel_l2_rest"] > 2 * clean["rel_l2_rest"]
+    assert st["rel_l2_heavy"] == clean["rel_l2_heavy"]
+    assert st["rel_l2"] < 0.2 * st["rel_l2_row_max"]
