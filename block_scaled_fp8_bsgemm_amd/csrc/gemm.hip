@@ -40,8 +40,8 @@
 // When K / 128 is even (the benchmark's K = 2048), the blockscale and mxfp8
 // GEMMs run as persistent kernels instead: one workgroup per CU walks several
 // tiles, so the workgroup launch is not paid per tile.  In the blockscale one
-// a finished tile's stores go out inside the next tile's first K block,
-// between its MFMAs (bit-identical results).
+// a finished tile's stores go out while the next tile's first operands land
+// and inside its first K block, between its MFMAs (bit-identical results).
 //
 // A second blockscale kernel reads B in a prepacked form (the same bytes in the
 // MFMA's operand order, written once by bprepack_kernel) straight into
@@ -896,32 +896,66 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
     store_tile<MODE>(acc, g, m0, n0, wave, lane);
 }
 
+// A plain tile's epilogue is split in two, so that neither end of a tile
+// boundary waits idle.  Its row groups 0 .. TAIL_RG - 1 are stored at the end
+// of the tile (tail_stores), behind the next tile's first DMA and while it
+// lands; the rest go out inside the next tile's first K block
+// (kblock_first).  TAIL_RG = 4 measured 1-2 % faster than 0, 2, 6 or 8.
+constexpr int TAIL_RG = 4;
+
+// The lane's two store offsets in a row group of a plain tile, in elements
+// (see store_tile), and its half.
+struct PlainOffsets {
+    uint32_t lx, ly;
+    bool up;
+};
+__device__ __forceinline__ PlainOffsets plain_offsets(int64_t N, int wm, int wn, int lane) {
+    asm volatile("" : "+v"(lane));   // formed here, per tile, not hoisted
+    PlainOffsets o;
+    o.up = (lane >> 3) & 1;
+    const int px = (lane >> 4) + (o.up ? 4 : 0);
+    o.lx = (uint32_t)((wm * WM + (lane & 7)) * N + wn * WN + px * 8);
+    o.ly = o.lx + (uint32_t)(8 * N + (o.up ? -32 : 32));
+    return o;
+}
+
+// Row group i of a plain tile (i a constant once the caller's loop is
+// unrolled), stored non-temporally through rC (a descriptor of C from the
+// tile's first element on), or through the zero-size descriptor, which
+// stores nothing but issues the same two instructions.
+__device__ __forceinline__ void plain_store_rg(const v4f (&acc)[TM][TN], int i, __amdgpu_buffer_rsrc_t rC,
+                                               int64_t N, const PlainOffsets &o) {
+    u32x4 x, y;
+    tile_pieces(acc, i, o.up, x, y);
+    const uint32_t ri = (uint32_t)(i * 16 * N);   // the row group's first element
+    __builtin_amdgcn_raw_buffer_store_b128(x, rC, 2 * (ri + o.lx), 0, 2);   // 2: nt
+    __builtin_amdgcn_raw_buffer_store_b128(y, rC, 2 * (ri + o.ly), 0, 2);
+}
+
 // The first K block of every tile in the persistent blockscale kernel.  It
 // carries no products over from a previous block, and the first fold of each
 // sub-tile, three MFMAs after its MFMA as in kblock, sets the accumulator to
 // fma(p, s, +0), which is what folding into a zeroed accumulator gives; the
 // last three sub-tiles, whose first fold is the next block's, are zeroed
-// once stored.  So the accumulators may still hold the previous tile when the
-// block starts:
-// if that tile was a plain one (see tile_is_plain), its epilogue goes out
-// here, the stores of its row group i just before MFMA 4 i, the last reads
-// of those accumulators.  The C stores so drain while the MFMAs of the new
-// tile run, not between tiles.  rC is a descriptor of the previous tile's
-// part of C from its first element on (row-major C: contiguous bands), or
-// the zero-size one when there is nothing to store: the stores are always
-// issued, so that every wave runs the same instructions and the vector
-// memory count below is exact.  lx and ly are the lane's two store offsets
-// in a row group and up its half (see store_tile), in elements.  The DMA of
-// block 1 goes out after MFMAs 0..8 as in kblock, before the stores of row
-// groups 3..6, so at the barrier before row group 7 this wave's DMA has
-// landed once at most those 8 stores are outstanding (vector memory
+// here.  So the accumulators may still hold the previous tile when the block
+// starts: if that tile was a plain one (see tile_is_plain), the stores of
+// its row group i >= TAIL_RG go out here, just before MFMA 4 i, the last
+// reads of those accumulators, and drain while the new tile's MFMAs run.  rC
+// is a descriptor of the previous tile's part of C from its first element
+// on (row-major C: contiguous bands), or the zero-size one when there is
+// nothing to store: the stores are always issued, so that every wave runs
+// the same instructions and the vector memory count below is exact.  The
+// DMA of block 1 goes out after MFMAs 0..8 as in kblock, before the stores of
+// row groups 4..6, so at the barrier before row group 7 this wave's DMA has
+// landed once at most those 6 stores are outstanding (vector memory
 // operations retire in issue order).
 template <int ST>
 __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
                                              v8i (&bf)[TN], float (&s)[TM], const Loader &L,
                                              const Panels &P, int kload, bool vload, int wm, int wn,
                                              int frow, int fc, __amdgpu_buffer_rsrc_t rC,
-                                             int64_t N, uint32_t lx, uint32_t ly, bool up) {
+                                             int64_t N, const PlainOffsets &o) {
+    static_assert(TAIL_RG >= 3 && TAIL_RG <= 6, "the wait below counts the stores of row groups TAIL_RG..6");
     const uint8_t *as = stA<ST>();
     v8i an = a;
     v8i a_next = a;
@@ -931,7 +965,8 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
         const v8i af = an;
         if (i + 1 < TM) an = lds_frag(as, wm * WM + (i + 1) * 16 + frow, fc);
         if (i == TM - 1) {
-            __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): the stores of row groups 3..6 may remain
+            // vmcnt(2 * (7 - TAIL_RG)): the stores of row groups TAIL_RG..6 may remain
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * (7 - TAIL_RG)));
             barrier_lds_only();
             a_next = lds_frag(stA<ST ^ 1>(), wm * WM + frow, fc);
             read_scales<ST ^ 1>(rn, wm, wn, frow);
@@ -939,18 +974,12 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 #pragma unroll
         for (int j = 0; j < TN; j++) {
             const int k = i * TN + j;
-            if (j == 0) {
-                u32x4 x, y;
-                tile_pieces(acc, i, up, x, y);
-                const uint32_t ri = (uint32_t)(i * 16 * N);   // the row group's first element
-                __builtin_amdgcn_raw_buffer_store_b128(x, rC, 2 * (ri + lx), 0, 2);   // 2: nt
-                __builtin_amdgcn_raw_buffer_store_b128(y, rC, 2 * (ri + ly), 0, 2);
-                if (i == TM - 1) {
-                    // products 29..31 are first folded by the next block, which
-                    // adds them (fma into the accumulator): start those at zero
+            if (j == 0 && i >= TAIL_RG) plain_store_rg(acc, i, rC, N, o);
+            if (j == 0 && i == TM - 1) {
+                // products 29..31 are first folded by the next block, which
+                // adds them (fma into the accumulator): start those at zero
 #pragma unroll
-                    for (int jj = 1; jj < TN; jj++) acc[i][jj] = (v4f){0.f, 0.f, 0.f, 0.f};
-                }
+                for (int jj = 1; jj < TN; jj++) acc[i][jj] = (v4f){0.f, 0.f, 0.f, 0.f};
             }
             p[k & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 bf[j], af, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
@@ -978,11 +1007,12 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
 // one stream.  After a tile's last K block (which always sits in stage 0)
 // the next tile's block 0 is DMA'd into stage 1, unread by then.  Blockscale:
-// a plain tile's epilogue then goes out inside the next tile's first K block
-// (kblock_first), between its MFMAs; the last tile and tiles that are not
-// plain store at once.  mxfp8: the epilogue stores C from the accumulators
-// while that DMA is in flight.  (A variant that issued the DMA from inside
-// the last K block spilled registers in the K loop.)
+// a plain tile then stores half of its row groups while that DMA lands and
+// the other half inside the next tile's first K block (kblock_first), between
+// its MFMAs; the last tile and tiles that are not plain store at once.
+// mxfp8: the epilogue stores C from the accumulators while that DMA is in
+// flight.  (Variants that issued the DMA from inside the last K block spilled
+// registers in the K loop.)
 template <int MODE>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
     constexpr bool MX = MODE == MODE_MX;
@@ -1046,16 +1076,11 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         } else {
             {
                 const GemmArgs gt = args();
-                int ln = lane;
-                asm volatile("" : "+v"(ln));   // form the store offsets here, per tile
-                const bool up = (ln >> 3) & 1;
-                const int px = (ln >> 4) + (up ? 4 : 0);
-                const uint32_t lx = (uint32_t)((wm * WM + (ln & 7)) * gt.N + wn * WN + px * 8);
-                const uint32_t ly = lx + (uint32_t)(8 * gt.N + (up ? -32 : 32));
+                const PlainOffsets o = plain_offsets(gt.N, wm, wn, lane);
                 const __amdgpu_buffer_rsrc_t rC =
                     pend ? make_rsrc(gt.C + pm0 * gt.N + pn0, (gt.M - pm0) * gt.N * 2) : L.rZ;
                 kblock_first<1>(acc, p, s_tail, a, bf, s, L, L.P, 1, true, wm, wn, frow, fc, rC,
-                                gt.N, lx, ly, up);
+                                gt.N, o);
             }
             kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, 2, 2 < KB, wm, wn, frow, fc);
             for (int kb = 2; kb < KB; kb += 2) {
@@ -1103,13 +1128,26 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 #pragma unroll
                 for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
         } else {
-            // A plain tile's stores go out inside the next tile's first K
-            // block; the last tile and other tiles store here.
+            // The last tile and tiles that are not plain store here.  A
+            // plain tile stores its row groups 0 .. TAIL_RG - 1 here, behind
+            // the next tile's DMA and while it lands, and the rest inside the
+            // next tile's first K block.  Every path issues those 2 * TAIL_RG
+            // stores (other tiles through the zero-size descriptor), so once
+            // at most that many are outstanding the DMA, and anything issued
+            // before it, has landed.
             const bool plain = tile_is_plain(args(), m0, n0);
             if (!has_next || !plain) store_tile<MODE>(acc, args(), m0, n0, wave, lane);
             if (!has_next) break;
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the next tile's block 0 has landed
-            __syncthreads();
+            {
+                const GemmArgs gt = args();
+                const PlainOffsets o = plain_offsets(gt.N, wm, wn, lane);
+                const __amdgpu_buffer_rsrc_t rT =
+                    plain ? make_rsrc(gt.C + m0 * gt.N + n0, (gt.M - m0) * gt.N * 2) : L.rZ;
+#pragma unroll
+                for (int i = 0; i < TAIL_RG; i++) plain_store_rg(acc, i, rT, gt.N, o);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * TAIL_RG));   // vmcnt(2 * TAIL_RG)
+            barrier_lds_only();
             read_head<1>(a, bf, s, wm, wn, frow, fc);
             pend = plain;
             pm0 = m0;
