@@ -95,7 +95,7 @@ __shared__ __attribute__((aligned(1024))) uint8_t sA1[BM * BK];
 __shared__ __attribute__((aligned(1024))) uint8_t sB0[BN * BK];
 __shared__ __attribute__((aligned(1024))) uint8_t sB1[BN * BK];
 // scales per stage, one dword per entry: blockscale: [0, 256) a_scale of the
-// tile's rows; [256, 512) four 64-entry slots filled by waves 4..7 with
+// tile's rows (in the order of sa_row); [256, 512) four 64-entry slots filled by waves 4..7 with
 // b_scale, of which entries 256 and 257 (the tile's two 128-column blocks) are
 // read.  mxfp8: [0, 256) the K block's 4 E8M0 bytes of each A row, [256, 512)
 // those of each B row.
@@ -267,13 +267,27 @@ struct RawScales {
     float sb;
 };
 
+// The a_scale slots hold the tile's 256 rows in the order p = 8 q + i for
+// row 128 (q / 16) + 16 i + q % 16 (see sa_row), so that a lane's 8 values
+// (q = 16 wm + frow) are contiguous: two 16-byte reads instead of eight.
+__device__ __forceinline__ int sa_row(int p) {
+    const int i = p & 7, q = p >> 3;
+    return (q >> 4) * WM + i * 16 + (q & 15);
+}
+
 template <int ST>
 __device__ __forceinline__ void read_scales(RawScales &r, int wm, int wn, int frow) {
     const float *sc = stS<ST>();
     // this wave's 64 columns lie inside one 128-column b_scale block
     r.sb = sc[BM + (wn >> 1)];   // wave 4's slot: entries BM, BM+1
+    typedef float v4s __attribute__((ext_vector_type(4)));
+    const v4s *q = (const v4s *)(sc + (wm * 16 + frow) * TM);
+    const v4s lo = q[0], hi = q[1];
 #pragma unroll
-    for (int i = 0; i < TM; i++) r.sa[i] = sc[wm * WM + i * 16 + frow];
+    for (int i = 0; i < 4; i++) {
+        r.sa[i] = lo[i];
+        r.sa[4 + i] = hi[i];
+    }
 }
 
 __device__ __forceinline__ void combine_scales(float (&s)[TM], const RawScales &r) {
@@ -641,8 +655,9 @@ __device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wa
     L.voffB = rowB * K + chunk * 16;
     L.voffB1 = L.voffB ^ 64;
     L.k4 = 4 * K;
+    // blockscale: waves 0..3 fetch a_scale in the slot order of sa_row
     L.soff = MODE == MODE_MX ? ((wave & 3) * 64 + lane) * (K / 32)
-                             : ((wave < 4 ? wave * 64 : 0) + lane) * g.KB * 4;
+                             : (wave < 4 ? sa_row(wave * 64 + lane) : lane) * g.KB * 4;
     L.sdst = wave * 256;
 }
 
