@@ -120,6 +120,31 @@ def test_gemm_band_layout(M, bands, pad):
     assert np.array_equal(out, expect)
 
 
+@pytest.mark.parametrize("M,bands,pad", [(8292, 1, 0), (8192, 4, 64)])
+def test_gemm_persistent_tile_transitions(M, bands, pad):
+    """The persistent kernel carries a plain tile's stores over into the next
+    tile (half at the tile's end, half inside the next tile's first K block)
+    and stores other tiles at once.  M = 8292: 33 x 17 tiles, about 2.2 per
+    workgroup, the last M-tile ragged, so workgroups pass between plain and
+    ragged tiles in both orders; M = 8192 with padded bands: no tile is
+    plain.  Every element against the exact product, and the band gaps
+    untouched."""
+    N, K = 4352, 256
+    qa, sa, qb, sb = operands(M, N, K, seed=11, heavy=True)
+    say(f"bsgemm_fp8 tile transitions M={M} bands={bands} pad={pad}")
+    band_rows = M // bands
+    stride = band_rows * N + pad
+    C = torch.empty((bands - 1) * stride + band_rows * N + pad, dtype=torch.bfloat16, device=device())
+    C.view(torch.int16).fill_(0x5A5A)
+    run(qa, sa, qb, sb, bands=bands, band_stride=stride if pad else 0, C=C)
+    raw = bits16(C)
+    got = np.concatenate([raw[d * stride: d * stride + band_rows * N] for d in range(bands)]).reshape(M, N)
+    gemm_accept(got, qa, sa, qb, sb, f"tile transitions M={M} bands={bands} pad={pad}")
+    if pad:
+        for d in range(bands):
+            assert np.all(raw[d * stride + band_rows * N: (d + 1) * stride] == 0x5A5A)
+
+
 @pytest.mark.parametrize("M,bands,pad_to", [(4096, 1, None), (16384, 8, None), (20000, 8, 20096)])
 def test_gemm_full_size(M, bands, pad_to):
     """The benchmark shapes (N=7168, K=2048, heavy rows), in the launch
