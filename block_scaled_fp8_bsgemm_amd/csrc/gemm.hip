@@ -267,11 +267,13 @@ struct RawScales {
     float sb;
 };
 
-// The a_scale slots hold the tile's 256 rows in the order p = 8 q + i for
-// row 128 (q / 16) + 16 i + q % 16 (see sa_row), so that a lane's 8 values
-// (q = 16 wm + frow) are contiguous: two 16-byte reads instead of eight.
+// The a_scale slots hold the tile's 256 rows so that a lane's 8 values
+// (row 128 wm + 16 i + frow, i = 0..7; q = 16 wm + frow) are two 16-byte
+// pieces, i = 0..3 at slot 4 q and i = 4..7 at slot 128 + 4 q: two reads
+// instead of eight, and consecutive lanes read consecutive 16-byte pieces
+// (no bank conflicts).  Slot p holds row sa_row(p).
 __device__ __forceinline__ int sa_row(int p) {
-    const int i = p & 7, q = p >> 3;
+    const int q = (p >> 2) & 31, i = ((p >> 7) << 2) | (p & 3);
     return (q >> 4) * WM + i * 16 + (q & 15);
 }
 
@@ -281,8 +283,8 @@ __device__ __forceinline__ void read_scales(RawScales &r, int wm, int wn, int fr
     // this wave's 64 columns lie inside one 128-column b_scale block
     r.sb = sc[BM + (wn >> 1)];   // wave 4's slot: entries BM, BM+1
     typedef float v4s __attribute__((ext_vector_type(4)));
-    const v4s *q = (const v4s *)(sc + (wm * 16 + frow) * TM);
-    const v4s lo = q[0], hi = q[1];
+    const v4s *q = (const v4s *)sc + (wm * 16 + frow);
+    const v4s lo = q[0], hi = q[32];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         r.sa[i] = lo[i];
