@@ -915,9 +915,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
 
 // A plain tile's epilogue is split in two, so that neither end of a tile
 // boundary waits idle.  Its row groups 0 .. TAIL_RG - 1 are stored at the end
-// of the tile (tail_stores), behind the next tile's first DMA and while it
-// lands; the rest go out inside the next tile's first K block
-// (kblock_first).  TAIL_RG = 4 measured 1-2 % faster than 0, 2, 6 or 8.
+// of the tile (in gemm_persistent, after the K loop), behind the next tile's
+// first DMA and while it lands; the rest go out inside the next tile's first
+// K block (kblock_first).  TAIL_RG = 4 measured 1-2 % faster than 0, 2, 6 or
+// 8.
 constexpr int TAIL_RG = 4;
 
 // The lane's two store offsets in a row group of a plain tile, in elements
