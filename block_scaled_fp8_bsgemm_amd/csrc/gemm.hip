@@ -540,13 +540,14 @@ __device__ __forceinline__ void kblock_pb(v4f (&acc)[TM][TN], v4f (&p)[4], float
 //
 // The next K block kb + 1 goes to the other stage, which nobody reads after
 // the previous block's barrier: its DMA is issued one instruction after each
-// of this block's first nine MFMAs.  After row group 6 (every fragment of this
+// of nine consecutive MFMAs from MFMA SHIFT on (0 or DMA_SHIFT, see
+// gemm_persistent).  After row group 6 (every fragment of this
 // stage is then in registers) each wave waits for its DMA and the waves meet
 // at a barrier; the reads of block kb + 1's first fragments and scales then go
 // out between the MFMAs of row group 7, so that its MFMAs find them landed.
 // After the last block the DMA goes nowhere and those reads fetch unused
 // values.
-template <int ST>
+template <int ST, int SHIFT = 0>
 __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
                                        v8i (&bf)[TN], float (&s)[TM], const Loader &L,
                                        const Panels &P, int kload, bool vload, int wm, int wn,
@@ -581,9 +582,9 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             }
             // the DMA of the next block (kload, normally kb + 1) into the
             // other stage (unread since the previous block's barrier), one
-            // instruction after each of the first nine MFMAs, away from the
-            // head reads of row group 7
-            dma_block<ST>(L, P, k, kload, vload);
+            // instruction after each of nine consecutive MFMAs from MFMA
+            // SHIFT on, away from the head reads of row group 7
+            if (k >= SHIFT) dma_block<ST>(L, P, k - SHIFT, kload, vload);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -1031,8 +1032,18 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 // mxfp8: the epilogue stores C from the accumulators while that DMA is in
 // flight.  (Variants that issued the DMA from inside the last K block spilled
 // registers in the K loop.)
-template <int MODE>
+// The blockscale kernel runs one copy of this body per row half of the wave
+// grid (WMC = wm, a compile-time constant: each wave executes straight-line
+// code with its row offsets folded), and the second half issues its K
+// blocks' DMA DMA_SHIFT MFMAs later than the first, so that the two waves of
+// a SIMD do not stall on DMA issue at the same time (together ≈ 3 % faster,
+// bit-identical; a shift of 8 was slower).  WMC = -1: one body, wm at run
+// time (mxfp8).
+constexpr int DMA_SHIFT = 4;
+
+template <int MODE, int WMC>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
+    constexpr int DSH = WMC == 1 ? DMA_SHIFT : 0;
     constexpr bool MX = MODE == MODE_MX;
     int vb = blockIdx.x;
     int64_t m0, n0;
@@ -1040,7 +1051,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep in SGPRs
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = WMC >= 0 ? WMC : wave >> 2;
+    const int wn = wave & 3;
     const int KB = g.KB;   // even, at least 2
     const int frow = lane & 15;
     const int fc = lane >> 4;   // the lane group: K chunks fc and fc + 4
@@ -1100,10 +1112,10 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
                 kblock_first<1>(acc, p, s_tail, a, bf, s, L, L.P, 1, true, wm, wn, frow, fc, rC,
                                 gt.N, o);
             }
-            kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, 2, 2 < KB, wm, wn, frow, fc);
+            kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, 2, 2 < KB, wm, wn, frow, fc);
             for (int kb = 2; kb < KB; kb += 2) {
-                kblock<1>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
-                kblock<0>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
+                kblock<1, DSH>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
+                kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
             }
         }
         // the next tile's block 0 goes to stage 1 (unread after the last
@@ -1178,10 +1190,12 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 }
 
 __global__ void __launch_bounds__(NTHREADS) bsgemm_persistent_kernel(GemmArgs g) {
-    gemm_persistent<MODE_BS>(g);
+    // wm = wave / 4 = threadIdx.x / 256, the same for every lane of a wave
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 8)) gemm_persistent<MODE_BS, 1>(g);
+    else gemm_persistent<MODE_BS, 0>(g);
 }
 __global__ void __launch_bounds__(NTHREADS) mxgemm_persistent_kernel(GemmArgs g) {
-    gemm_persistent<MODE_MX>(g);
+    gemm_persistent<MODE_MX, -1>(g);
 }
 
 __global__ void __launch_bounds__(NTHREADS) bsgemm_tile_kernel(GemmArgs g) { gemm_tile<MODE_BS>(g); }
