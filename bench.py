@@ -28,7 +28,11 @@ K=512..4096 fitted as fixed + per-K-block cost.  `cpu_baseline` is the CPU
 oracle timed on a bounded row sample of the same workload and projected to a
 full step; the same leg checks those rows of the last timed step's C against
 the oracle (every element inside the bound the fp8 MFMA allows around the
-exact product) and reports it as `validated`.
+exact product) and reports it as `validated`.  After that line, stderr gets
+one `RESULT_JSON` record per (configuration, phase) with the median, the
+rate and its roofline share; `streaming.copy_kernel` (a plain copy through
+the library's streaming path) and `streaming.device_copy_runtime` (the
+runtime's blit) are the practical HBM ceilings.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
@@ -305,6 +309,32 @@ def streaming_rates(M, N, P, dev, iters=20):
     out["mxq_e4m3"] = rec(t, M * K * 3 + M * (K // 32))
     del aq_x, aq_q, aq_s, mq_s
     torch.cuda.empty_cache()
+    # practical ceilings: a plain copy through this library's streaming path
+    # (band_reduce of a single part: 16-byte non-temporal loads and stores,
+    # bf16 in and the same bf16 out), [16384,7168] bf16 = 235 MB per call, 2
+    # sets; and the runtime's device copy (a blit kernel), 512 MiB per call
+    nset = 2
+    cp_in = [torch.randn(M, N, device=dev).to(torch.bfloat16) for _ in range(nset)]
+    cp_out = [torch.empty(M, N, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
+    t = timed(lambda i: bs.band_reduce([cp_in[i]], cp_out[i]), nset)
+    out["copy_kernel"] = rec(t, 2 * M * N * 2)
+    del cp_in, cp_out
+    # the same copy at the row quantizer's size, [2048,7168] bf16 (59 MB per
+    # call), over 8 sets: the ceiling for a kernel of that size
+    nset = 8
+    cp_in = [torch.randn(band_rows, N, device=dev).to(torch.bfloat16) for _ in range(nset)]
+    cp_out = [torch.empty(band_rows, N, dtype=torch.bfloat16, device=dev) for _ in range(nset)]
+    t = timed(lambda i: bs.band_reduce([cp_in[i]], cp_out[i]), nset)
+    out["copy_kernel_band"] = rec(t, 2 * band_rows * N * 2)
+    del cp_in, cp_out
+    nset = 2
+    n = 1 << 27
+    cp_src = [torch.ones(n, dtype=torch.float32, device=dev) for _ in range(nset)]
+    cp_dst = [torch.empty(n, dtype=torch.float32, device=dev) for _ in range(nset)]
+    t = timed(lambda i: cp_dst[i].copy_(cp_src[i]), nset)
+    out["device_copy_runtime"] = rec(t, 2 * n * 4)
+    del cp_src, cp_dst
+    torch.cuda.empty_cache()
     return out
 
 
@@ -484,7 +514,8 @@ def cpu_baseline(ops, c_dev, M, N, K, P, target_s=10.0):
             "sample": f"GEMM on the first {R} of {M} rows ({tg:.2f} s, scaled x{M / R:.2f}); reduce and quantize "
                       f"of one full [{band_rows},{N}] band ({tr:.2f} s, {tq:.2f} s); dequantize of "
                       f"{band_rows} rows scaled x{M // band_rows} ({td:.2f} s projected)",
-            "projected_step_s": step_s}
+            "projected_step_s": step_s, "projected_gemm_s": tg * (M / R),
+            "projected_reduce_quantize_s": tr + tq, "projected_dequantize_s": td}
     t0 = time.perf_counter()
     st = bounds.check_bsgemm(c_dev[:R], acc, qa[:R], sa[:R], qb, sb)
     say(f"validated {R} rows in {time.perf_counter() - t0:.1f} s: {st}")
@@ -495,6 +526,73 @@ def cpu_baseline(ops, c_dev, M, N, K, P, target_s=10.0):
            "check": "every element of the last timed step's C on these rows inside the interval the fp8 "
                     "MFMA's truncation and rounding allow around the oracle's exact product"}
     return base, val
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def result_records(rec):
+    """One record per (configuration, phase) of the workload statement, with the
+    measured median, rate and roofline share; printed on stderr after the
+    JSON line (stdout carries that one line only).  Fields the bench does not
+    measure are null (bitexactness is the tests' job; the clock comes from
+    the counter profiles)."""
+    cores = (rec.get("cpu_baseline") or {}).get("cores") or os.cpu_count()
+    common = {"host_cores": cores, "cpu_model": cpu_model(), "sclk_mhz": None, "bitexact": None}
+    val = rec.get("validated") or {}
+    oracle_s = (rec.get("cpu_baseline") or {}).get("projected_step_s")
+    out = []
+
+    def add(config, phase, M, N, K, us, tflops=None, gbps=None, pct=None, **kw):
+        r = {"config": config, "phase": phase, "M": M, "N": N, "K": K, "time_us_median": us,
+             "tflops": tflops, "gbps": gbps, "pct_roofline": pct, "rel_l2": None, "validated": None,
+             "oracle_time_s": None}
+        r.update(common)
+        r.update(kw)
+        out.append(r)
+
+    ph = rec["phases"]
+    cb = rec.get("cpu_baseline") or {}
+    add("full_chunk_16384", "gemm", 16384, 7168, 2048, ph["gemm"]["median_us"],
+        tflops=ph["gemm"]["TFLOP/s"], pct=100 * ph["gemm"]["frac_fp8_peak"],
+        rel_l2=val.get("rel_l2_vs_exact"), validated=val.get("ok"), oracle_time_s=cb.get("projected_gemm_s"))
+    add("reduce_wire_16384", "reduce_quantize", 2048, 7168, None, ph["reduce_quantize"]["median_us"],
+        gbps=ph["reduce_quantize"]["GB/s"], pct=100 * ph["reduce_quantize"]["frac_hbm"],
+        oracle_time_s=cb.get("projected_reduce_quantize_s"))
+    add("reduce_wire_16384", "dequantize", 16384, 7168, None, ph["dequantize"]["median_us"],
+        gbps=ph["dequantize"]["GB/s"], pct=100 * ph["dequantize"]["frac_hbm"],
+        oracle_time_s=cb.get("projected_dequantize_s"))
+    add("full_chunk_16384", "step", 16384, 7168, 2048, rec["ms_per_step"] * 1e3, tflops=rec["step_tflops"],
+        oracle_time_s=oracle_s)
+    if "gemm_m4096" in rec:
+        g = rec["gemm_m4096"]
+        add("prefill_chunk_4096", "gemm", 4096, 7168, 2048, g["median_us"], tflops=g["TFLOP/s"],
+            pct=100 * g["frac_fp8_peak"])
+    for name, d in (rec.get("streaming") or {}).items():
+        rows, N = {"rowdq_e4m3": (16384, 7168), "actq_e4m3": (16384, 2048), "mxq_e4m3": (16384, 2048),
+                   "copy_kernel": (16384, 7168), "copy_kernel_band": (2048, 7168),
+                   "device_copy_runtime": (None, None)}.get(name, (2048, 7168))
+        add("hbm_ceiling" if "copy" in name else "streaming_alone", name, rows, N, None, d["us"],
+            gbps=d["GB/s"], pct=100 * d["frac_hbm"])
+    if "mxfp8_gemm" in rec:
+        m = rec["mxfp8_gemm"]
+        add("mxfp8_16384x5120", "gemm", m["M"], m["N"], m["K"], m["us"], tflops=m["TFLOP/s"],
+            pct=100 * m["frac_fp8_peak"])
+    for key, d in (rec.get("pipeline_sweep") or {}).items():
+        Mp = d["M_padded"]
+        for phase, us in d["phases_median_us"].items():
+            kw = {"tflops": 2.0 * Mp * 7168 * 2048 / (us * 1e-6) / 1e12} if phase == "gemm" else {}
+            add(f"pipeline_{key}", phase, Mp, 7168, 2048, us, **kw)
+        add(f"pipeline_{key}", "step", Mp, 7168, 2048, d["us_per_step"])
+    return out
 
 
 def main():
@@ -613,6 +711,8 @@ def main():
         say("cpu_baseline (oracle on a row sample) and the check of the last step's C")
         rec["cpu_baseline"], rec["validated"] = cpu_baseline(last_ops, last_c, M, N, K, P)
     print(json.dumps(rec), flush=True)
+    for r in result_records(rec):
+        print("RESULT_JSON " + json.dumps(r), file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":
