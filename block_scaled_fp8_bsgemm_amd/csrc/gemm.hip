@@ -1029,8 +1029,8 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 // a plain tile then stores half of its row groups while that DMA lands and
 // the other half inside the next tile's first K block (kblock_first), between
 // its MFMAs; the last tile and tiles that are not plain store at once.
-// mxfp8: the epilogue stores C from the accumulators while that DMA is in
-// flight.  (Variants that issued the DMA from inside the last K block spilled
+// mxfp8: the epilogue stores C from the accumulators behind that DMA, and
+// the stores drain under the next tile's first K block.  (Variants that issued the DMA from inside the last K block spilled
 // registers in the K loop.)
 // The blockscale kernel runs one copy of this body per row half of the wave
 // grid (WMC = wm, a compile-time constant: each wave executes straight-line
@@ -1139,19 +1139,26 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         }
 
         if constexpr (MX) {
-            store_tile<MODE>(acc, args(), m0, n0, wave, lane);
+            // The last tile and tiles that are not plain store here.  Every
+            // other tile stores its 2 * TM pieces behind the next tile's DMA
+            // (other tiles issue the same instructions through the zero-size
+            // descriptor, so that the count is exact on every path): once no
+            // more than those are outstanding, the DMA has landed, and the
+            // stores drain under the next tile's first K block.
+            const bool plain = tile_is_plain(args(), m0, n0);
+            if (!has_next || !plain) store_tile<MODE>(acc, args(), m0, n0, wave, lane);
             if (!has_next) break;
-            // Wait for the next tile's block 0 only: its DMA went out before
-            // this tile's stores, and vector memory operations retire in
-            // issue order, so once no more than the 2 * TM stores of a plain
-            // tile are outstanding, the DMA has landed.  The stores drain
-            // under the next tile's first K block instead.  Other tiles skip
-            // stores per lane and wait for everything.
-            if (tile_is_plain(args(), m0, n0))
-                __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16)
-            else
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            __syncthreads();
+            {
+                const GemmArgs gt = args();
+                const PlainOffsets o = plain_offsets(gt.N, wm, wn, lane);
+                const __amdgpu_buffer_rsrc_t rT =
+                    plain ? make_rsrc(gt.C + m0 * gt.N + n0, (gt.M - m0) * gt.N * 2) : L.rZ;
+#pragma unroll
+                for (int i = 0; i < TM; i++) plain_store_rg(acc, i, rT, gt.N, o);
+            }
+            static_assert(2 * TM == 16, "the wait below is vmcnt(16)");
+            __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): vmcnt[5:4] sit in bits 15:14
+            barrier_lds_only();
             read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
 #pragma unroll
             for (int i = 0; i < TM; i++)

@@ -87,6 +87,30 @@ def test_mxgemm_many_tiles_vs_oracle():
     mx_accept(bits16(C).reshape(M, N), qa, ea, qb, eb, f"mx many tiles M={M}")
 
 
+@pytest.mark.parametrize("M,bands,pad", [(8292, 1, 0), (8192, 4, 64)])
+def test_mxgemm_persistent_tile_transitions(M, bands, pad):
+    """The persistent kernel stores a plain tile behind the next tile's DMA
+    and lets those stores drain under its first K block; other tiles store
+    at once.  M = 8292: 33 x 17 tiles, about 2.2 per workgroup, the last
+    M-tile ragged, so workgroups pass between plain and ragged tiles in both
+    orders; M = 8192 with padded bands: no tile is plain.  Every element
+    against the exact product, and the band gaps untouched."""
+    N, K = 4352, 256
+    qa, ea, qb, eb = operands(M, N, K, seed=12, heavy=True)
+    say(f"mxgemm_fp8 tile transitions M={M} bands={bands} pad={pad}")
+    band_rows = M // bands
+    stride = band_rows * N + pad
+    C = torch.empty((bands - 1) * stride + band_rows * N + pad, dtype=torch.bfloat16, device=device())
+    C.view(torch.int16).fill_(0x5A5A)
+    run(qa, ea, qb, eb, bands=bands, band_stride=stride if pad else 0, C=C)
+    raw = bits16(C)
+    got = np.concatenate([raw[d * stride: d * stride + band_rows * N] for d in range(bands)]).reshape(M, N)
+    mx_accept(got, qa, ea, qb, eb, f"mx tile transitions M={M} bands={bands} pad={pad}", model=False)
+    if pad:
+        for d in range(bands):
+            assert np.all(raw[d * stride + band_rows * N: (d + 1) * stride] == 0x5A5A)
+
+
 def test_mxgemm_unit_scales_exact():
     """Small codes, every scale byte 127: all sums are exact in fp32, so the
     device result equals the oracle bit for bit."""
