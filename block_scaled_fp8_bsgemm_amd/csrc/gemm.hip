@@ -169,24 +169,32 @@ struct Loader {
     int sdst;    // byte offset of this wave's 256-byte scale slot
 };
 
+// A tile's byte offsets in A, in B and in this wave's scales, or the change
+// of them from one tile to another (persistent blockscale kernel).
+struct TileOff {
+    int a, b, s;
+};
+
 // One DMA instruction of a stage load: pieces 0..7 are the A and B slots
 // i = piece / 2 (A for even pieces, B for odd), piece 8 the scales.  A block
 // past the end (valid == false) goes through the zero-size descriptor: the
-// loads touch no memory and the stage is not read again.
+// loads touch no memory and the stage is not read again.  d moves the
+// lanes' offsets to another tile of the same whole-matrix descriptors.
 template <int ST, int PIECE>
-__device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int kb, bool valid) {
+__device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int kb, bool valid,
+                                          const TileOff &d = TileOff{0, 0, 0}) {
     const int koff = kb * BK;
     if (PIECE < 8) {
         const int i = PIECE >> 1;
         const int q = L.ldsq + i * 1024;
         if (PIECE & 1) {
             // B: slot i's global rows are those of slot 0 plus 0, 8, 4, 12
-            const int vo = ((i & 1) ? L.voffB1 : L.voffB) + (2 * (i & 1) + (i >> 1)) * L.k4;
+            const int vo = ((i & 1) ? L.voffB1 : L.voffB) + (2 * (i & 1) + (i >> 1)) * L.k4 + d.b;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rB : L.rZ, (lds_void *)(stB<ST>() + q),
                                                      16, vo, koff, 0, 0);
         } else {
             // A: slot i's rows are those of slot 0 plus 0, 4, 16, 20 (see load_stage)
-            const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4;
+            const int vo = ((i & 1) ? L.voff1 : L.voff) + (4 * (i >> 1) + (i & 1)) * L.k4 + d.a;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rA : L.rZ, (lds_void *)(stA<ST>() + q),
                                                      16, vo, koff, 0, 0);
         }
@@ -198,7 +206,7 @@ __device__ __forceinline__ void dma_piece(const Loader &L, const Panels &P, int 
         // 256-byte slot; no branch: every wave issues exactly one.
         __builtin_amdgcn_raw_ptr_buffer_load_lds(valid ? P.rS : L.rZ,
                                                  (lds_void *)((uint8_t *)stS<ST>() + L.sdst), 4,
-                                                 L.soff, kb * 4, 0, 0);
+                                                 L.soff + d.s, kb * 4, 0, 0);
     }
 }
 
@@ -380,17 +388,18 @@ __device__ __forceinline__ void read_head_mx(v8i &a, v8i (&bf)[TN], MxScales &x,
 // kb (see kblock); dma_block takes the block, its validity and the tile's
 // panels explicitly.
 template <int ST>
-__device__ __forceinline__ void dma_block(const Loader &L, const Panels &P, int k, int kload, bool v) {
+__device__ __forceinline__ void dma_block(const Loader &L, const Panels &P, int k, int kload, bool v,
+                                          const TileOff &d = TileOff{0, 0, 0}) {
     if (k < 9) {
-        if (k == 0) dma_piece<ST ^ 1, 8>(L, P, kload, v);
-        if (k == 1) dma_piece<ST ^ 1, 0>(L, P, kload, v);
-        if (k == 2) dma_piece<ST ^ 1, 1>(L, P, kload, v);
-        if (k == 3) dma_piece<ST ^ 1, 2>(L, P, kload, v);
-        if (k == 4) dma_piece<ST ^ 1, 3>(L, P, kload, v);
-        if (k == 5) dma_piece<ST ^ 1, 4>(L, P, kload, v);
-        if (k == 6) dma_piece<ST ^ 1, 5>(L, P, kload, v);
-        if (k == 7) dma_piece<ST ^ 1, 6>(L, P, kload, v);
-        if (k == 8) dma_piece<ST ^ 1, 7>(L, P, kload, v);
+        if (k == 0) dma_piece<ST ^ 1, 8>(L, P, kload, v, d);
+        if (k == 1) dma_piece<ST ^ 1, 0>(L, P, kload, v, d);
+        if (k == 2) dma_piece<ST ^ 1, 1>(L, P, kload, v, d);
+        if (k == 3) dma_piece<ST ^ 1, 2>(L, P, kload, v, d);
+        if (k == 4) dma_piece<ST ^ 1, 3>(L, P, kload, v, d);
+        if (k == 5) dma_piece<ST ^ 1, 4>(L, P, kload, v, d);
+        if (k == 6) dma_piece<ST ^ 1, 5>(L, P, kload, v, d);
+        if (k == 7) dma_piece<ST ^ 1, 6>(L, P, kload, v, d);
+        if (k == 8) dma_piece<ST ^ 1, 7>(L, P, kload, v, d);
     }
 }
 template <int ST>
@@ -545,13 +554,15 @@ __device__ __forceinline__ void kblock_pb(v4f (&acc)[TM][TN], v4f (&p)[4], float
 // stage is then in registers) each wave waits for its DMA and the waves meet
 // at a barrier; the reads of block kb + 1's first fragments and scales then go
 // out between the MFMAs of row group 7, so that its MFMAs find them landed.
-// After the last block the DMA goes nowhere and those reads fetch unused
-// values.
+// The block loaded is block kload of the panels P, moved by d to another
+// tile: the persistent kernel's last block of a tile loads the next tile's
+// block 0, whose head it then reads.  After the last tile the DMA goes
+// nowhere and those reads fetch unused values.
 template <int ST, int SHIFT = 0>
 __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s_tail, v8i &a,
                                        v8i (&bf)[TN], float (&s)[TM], const Loader &L,
                                        const Panels &P, int kload, bool vload, int wm, int wn,
-                                       int frow, int fc) {
+                                       int frow, int fc, const TileOff &d = TileOff{0, 0, 0}) {
     const uint8_t *as = stA<ST>();
     v8i an = a;
     v8i a_next = a;
@@ -584,7 +595,7 @@ __device__ __forceinline__ void kblock(v4f (&acc)[TM][TN], v4f (&p)[4], float &s
             // other stage (unread since the previous block's barrier), one
             // instruction after each of nine consecutive MFMAs from MFMA
             // SHIFT on, away from the head reads of row group 7
-            if (k >= SHIFT) dma_block<ST>(L, P, k - SHIFT, kload, vload);
+            if (k >= SHIFT) dma_block<ST>(L, P, k - SHIFT, kload, vload, d);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -662,6 +673,38 @@ __device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wa
     L.soff = MODE == MODE_MX ? ((wave & 3) * 64 + lane) * (K / 32)
                              : (wave < 4 ? sa_row(wave * 64 + lane) : lane) * g.KB * 4;
     L.sdst = wave * 256;
+}
+
+// The persistent blockscale kernel's descriptors cover whole matrices (each
+// under 2^31 bytes, which the host checks), and a tile is a byte offset in
+// the lanes' offsets: range-checked like them, so rows past the end still
+// read zeros, and a tile change needs no new descriptor.
+template <int MODE>
+__device__ __forceinline__ Panels whole_panels(const GemmArgs &g, int wave) {
+    Panels P;
+    P.rA = make_rsrc(g.A, g.M * g.K);
+    P.rB = make_rsrc(g.B, g.N * g.K);
+    P.rS = wave < 4 ? make_rsrc(g.sa, g.M * g.KB * 4) : make_rsrc(g.sb, (int64_t)g.NB * g.KB * 4);
+    return P;
+}
+
+// Tile (m0, n0)'s offsets for whole_panels: A's and B's row panels, and the
+// scales this wave fetches (a_scale rows for waves 0..3, b_scale column
+// blocks for 4..7).
+__device__ __forceinline__ TileOff tile_off(const GemmArgs &g, int64_t m0, int64_t n0, int wave) {
+    TileOff t;
+    t.a = (int)(m0 * g.K);
+    t.b = (int)(n0 * g.K);
+    t.s = wave < 4 ? (int)(m0 * g.KB * 4) : (int)((n0 / 128) * g.KB * 4);
+    return t;
+}
+
+__device__ __forceinline__ void shift_loader(Loader &L, const TileOff &d) {
+    L.voff += d.a;
+    L.voff1 += d.a;
+    L.voffB += d.b;
+    L.voffB1 += d.b;
+    L.soff += d.s;
 }
 
 // Where the epilogue's stores go.  Row m0 + ml of a tile lies in band
@@ -1024,14 +1067,17 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 // One workgroup per CU walks the tiles of virtual workgroups b, b + G,
 // b + 2G, ... (G = grid size, a multiple of 8, so every tile stays on the XCD
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
-// one stream.  After a tile's last K block (which always sits in stage 0)
-// the next tile's block 0 is DMA'd into stage 1, unread by then.  Blockscale:
-// a plain tile then stores half of its row groups while that DMA lands and
-// the other half inside the next tile's first K block (kblock_first), between
-// its MFMAs; the last tile and tiles that are not plain store at once.
-// mxfp8: the epilogue stores C from the accumulators behind that DMA, and
-// the stores drain under the next tile's first K block.  (Variants that issued the DMA from inside the last K block spilled
-// registers in the K loop.)
+// one stream; block 0 of every tile sits in stage 1, its last block in stage
+// 0.  Blockscale: the descriptors cover whole matrices, so the last K block
+// of a tile DMAs the next tile's block 0 (its lanes' offsets moved by dn) as
+// any block DMAs its successor, and reads its head; a plain tile then stores
+// half of its row groups at once and the other half inside the next tile's
+// first K block (kblock_first), between its MFMAs; the last tile and tiles
+// that are not plain store everything at once.  (Switching descriptors
+// inside the K loop instead made the compiler spill hundreds of VGPRs.)
+// mxfp8: after the last K block, the next tile's block 0 is DMA'd into stage
+// 1, the epilogue stores C from the accumulators behind that DMA, and the
+// stores drain under the next tile's first K block.
 // The blockscale kernel runs one copy of this body per row half of the wave
 // grid (WMC = wm, a compile-time constant: each wave executes straight-line
 // code with its row offsets folded), and the second half issues its K
@@ -1059,7 +1105,12 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 
     Loader L;
     init_loader<MODE>(L, g, wave, lane);
-    L.P = panels_of<MODE>(g, m0, n0, wave);
+    if constexpr (MX) {
+        L.P = panels_of<MODE>(g, m0, n0, wave);
+    } else {
+        L.P = whole_panels<MODE>(g, wave);
+        shift_loader(L, tile_off(g, m0, n0, wave));
+    }
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -1097,6 +1148,24 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
     // that tile's origin
     bool pend = false;
     int64_t pm0 = 0, pn0 = 0;
+    // the tile after this one and, blockscale, the move of the loader's
+    // offsets from this tile to it (zero if there is none); found at the
+    // tile boundary, so that only three offsets stay live across the K loop
+    int64_t m0n = 0, n0n = 0;
+    bool has_next = false;
+    TileOff dn = {0, 0, 0};
+    auto find_next = [&]() {
+        const GemmArgs gt = args();
+        has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
+        dn = TileOff{0, 0, 0};
+        if (has_next) {
+            const TileOff tn = tile_off(gt, m0n, n0n, wave), tc = tile_off(gt, m0, n0, wave);
+            dn.a = __builtin_amdgcn_readfirstlane(tn.a - tc.a);
+            dn.b = __builtin_amdgcn_readfirstlane(tn.b - tc.b);
+            dn.s = __builtin_amdgcn_readfirstlane(tn.s - tc.s);
+        }
+    };
+    if constexpr (!MX) find_next();
     for (;;) {
         if constexpr (MX) {
             for (int kb = 0; kb < KB; kb += 2) {
@@ -1112,18 +1181,23 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
                 kblock_first<1>(acc, p, s_tail, a, bf, s, L, L.P, 1, true, wm, wn, frow, fc, rC,
                                 gt.N, o);
             }
-            kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, 2, 2 < KB, wm, wn, frow, fc);
+            // The last block (always in stage 0) DMAs the next tile's block
+            // 0 into stage 1, as any block DMAs its successor, and its head
+            // reads fetch that block's first fragments and scales.
+            const TileOff d0 = {0, 0, 0};
+            kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, 2 < KB ? 2 : 0, 2 < KB || has_next, wm, wn,
+                           frow, fc, 2 < KB ? d0 : dn);
             for (int kb = 2; kb < KB; kb += 2) {
                 kblock<1, DSH>(acc, p, s_tail, a, bf, s, L, L.P, kb + 1, true, wm, wn, frow, fc);
-                kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2, kb + 2 < KB, wm, wn, frow, fc);
+                kblock<0, DSH>(acc, p, s_tail, a, bf, s, L, L.P, kb + 2 < KB ? kb + 2 : 0,
+                               kb + 2 < KB || has_next, wm, wn, frow, fc, kb + 2 < KB ? d0 : dn);
             }
+            shift_loader(L, dn);
         }
-        // the next tile's block 0 goes to stage 1 (unread after the last
-        // block's barrier but for head reads whose values are never used)
-        // while this tile's epilogue stores
-        int64_t m0n = 0, n0n = 0;
-        bool has_next;
-        {
+        // mxfp8: the next tile's block 0 goes to stage 1 (unread after the
+        // last block's barrier but for head reads whose values are never
+        // used) while this tile's epilogue stores
+        if constexpr (MX) {
             const GemmArgs gt = args();
             has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
             if (has_next) {
@@ -1166,12 +1240,12 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
                 for (int j = 0; j < TN; j++) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
         } else {
             // The last tile and tiles that are not plain store here.  A
-            // plain tile stores its row groups 0 .. TAIL_RG - 1 here, behind
-            // the next tile's DMA and while it lands, and the rest inside the
-            // next tile's first K block.  Every path issues those 2 * TAIL_RG
-            // stores (other tiles through the zero-size descriptor), so once
-            // at most that many are outstanding the DMA, and anything issued
-            // before it, has landed.
+            // plain tile stores its row groups 0 .. TAIL_RG - 1 here and the
+            // rest inside the next tile's first K block.  Every path issues
+            // those 2 * TAIL_RG stores (other tiles through the zero-size
+            // descriptor), so that the vector memory count of the next
+            // tile's first block is exact.  The next tile's block 0 and its
+            // head are already in (the last K block loaded them).
             const bool plain = tile_is_plain(args(), m0, n0);
             if (!has_next || !plain) store_tile<MODE>(acc, args(), m0, n0, wave, lane);
             if (!has_next) break;
@@ -1183,9 +1257,6 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 #pragma unroll
                 for (int i = 0; i < TAIL_RG; i++) plain_store_rg(acc, i, rT, gt.N, o);
             }
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * TAIL_RG));   // vmcnt(2 * TAIL_RG)
-            barrier_lds_only();
-            read_head<1>(a, bf, s, wm, wn, frow, fc);
             pend = plain;
             pm0 = m0;
             pn0 = n0;
@@ -1193,6 +1264,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         vb += (int)gridDim.x;
         m0 = m0n;
         n0 = n0n;
+        if constexpr (!MX) find_next();
     }
 }
 
@@ -1283,7 +1355,10 @@ int bs_launch_gemm(const uint8_t *A, const float *sa, const uint8_t *B, const fl
                    uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                    int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
-    if (g.KB % 2 == 0)
+    // The persistent kernel addresses each operand through one descriptor
+    // with 31-bit lane offsets, the rows of a ragged last tile included.
+    const int64_t lim = 0x7FFFFFFF;
+    if (g.KB % 2 == 0 && (M + BM) * K <= lim && (N + BN) * K <= lim)
         return bs_enqueue(bsgemm_persistent_kernel, dim3(persistent_grid(g, stream)), dim3(NTHREADS),
                           stream, g);
     return bs_enqueue(bsgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);

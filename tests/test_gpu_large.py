@@ -1,6 +1,7 @@
 """Maximum-size cases on the device (an MI355X holds 288 GB): the dequantizer
-past 2^31 packs, where it switches to 64-bit indices, and the GEMM with a
-14 GiB output written as 8 bands, where row offsets pass 2^32 bytes.  Inputs
+past 2^31 packs, where it switches to 64-bit indices, the GEMM with a
+14 GiB output written as 8 bands, where row offsets pass 2^32 bytes, and the
+GEMM with an operand of more than 2^31 bytes.  Inputs
 are drawn on the device; sampled outputs (whole rows for the GEMM) are
 checked against the oracle, so nothing large crosses to the host."""
 import numpy as np
@@ -62,3 +63,35 @@ def test_gemm_output_past_4gib():
     del C, qa, sa
     torch.cuda.empty_cache()
     gemm_accept_rows(got, rows, qa_h, sa_h, qb_h, sb_h, f"M={M} {rows.size} whole rows")
+
+
+def test_gemm_operand_past_2gib():
+    """A of 2^31 bytes and more (M = 2^20 + 128, K = 2048): past what one
+    31-bit descriptor offset reaches, so the host takes the tile kernel,
+    whose descriptors start at each tile.  Whole rows on both sides of byte
+    2^31 of A against the oracle."""
+    M, N, K = (1 << 20) + 128, 256, 2048
+    KB = K // 128
+    dev = device()
+    say(f"bsgemm_fp8 M={M} N={N} K={K} (A of {M * K} bytes)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(23)
+    qa = torch.randint(0, 0x7F, (M, K), dtype=torch.uint8, device=dev, generator=g)   # no NaN codes
+    qa |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    sa = torch.rand((M, KB), device=dev, generator=g) * 2.0 ** -8
+    qb, sb = bs.blockq_e4m3(0.02 * torch.randn(N, K, device=dev, generator=g), 128)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    C.view(torch.int16).fill_(0x7FC0)
+    bs.bsgemm_fp8(qa, sa, qb, sb, C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    split = (1 << 31) // K                     # the first row at or past byte 2^31 of A
+    edge = [0, split - 1, split, split + 1, M - 129, M - 128, M - 1]
+    rows = np.unique(np.concatenate([rng.integers(0, M, 40), edge])).astype(np.int64)
+    tm = torch.from_numpy(rows).to(dev)
+    got = C.view(M, N)[tm].view(torch.int16).cpu().numpy().view(np.uint16)
+    qa_r, sa_r = qa[tm].cpu().numpy(), sa[tm].cpu().numpy()
+    qb_h, sb_h = qb.cpu().numpy(), sb.cpu().numpy()
+    del C, qa, sa
+    torch.cuda.empty_cache()
+    gemm_accept_rows(got, np.arange(rows.size), qa_r, sa_r, qb_h, sb_h, f"M={M} {rows.size} whole rows")
