@@ -170,7 +170,7 @@ struct Loader {
 };
 
 // A tile's byte offsets in A, in B and in this wave's scales, or the change
-// of them from one tile to another (persistent blockscale kernel).
+// of them from one tile to another (persistent kernels).
 struct TileOff {
     int a, b, s;
 };
@@ -402,20 +402,17 @@ __device__ __forceinline__ void dma_block(const Loader &L, const Panels &P, int 
         if (k == 8) dma_piece<ST ^ 1, 7>(L, P, kload, v, d);
     }
 }
-template <int ST>
-__device__ __forceinline__ void dma_next(const Loader &L, int k, int kb, int KB) {
-    dma_block<ST>(L, L.P, k, kb + 1, kb + 1 < KB);
-}
 
 // One mxfp8 K block from stage ST: the same schedule as the blockscale kblock
 // below (A fragments one row group ahead, barrier after row group 6, the next
-// block's head read between the MFMAs of row group 7, its DMA during the
-// first nine MFMAs), but the block scales are applied inside the MFMA and
-// each MFMA accumulates straight into its accumulator: no fold.
+// block's head read between the MFMAs of row group 7, its DMA of block kload
+// (moved by d to another tile) during the first nine MFMAs), but the block
+// scales are applied inside the MFMA and each MFMA accumulates straight into
+// its accumulator: no fold.
 template <int ST>
 __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[TN], MxScales &x,
-                                          const Loader &L, int kb, int KB, int wm, int wn, int frow,
-                                          int g) {
+                                          const Loader &L, int kload, bool vload, int wm, int wn,
+                                          int frow, int g, const TileOff &d = TileOff{0, 0, 0}) {
     const uint8_t *as = stA<ST>();
     v8i an = a;
     v8i a_next = a;
@@ -434,7 +431,7 @@ __device__ __forceinline__ void kblock_mx(v4f (&acc)[TM][TN], v8i &a, v8i (&bf)[
             const int k = i * TN + j;
             acc[i][j] = mx_mfma(bf[j], af, acc[i][j], x, i, j);
             if (i == TM - 1) bf[j] = lds_frag(stB<ST ^ 1>(), wn * WN + j * 16 + frow, g);
-            dma_next<ST>(L, k, kb, KB);
+            dma_block<ST>(L, L.P, k, kload, vload, d);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -675,7 +672,7 @@ __device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wa
     L.sdst = wave * 256;
 }
 
-// The persistent blockscale kernel's descriptors cover whole matrices (each
+// The persistent kernels' descriptors cover whole matrices (each
 // under 2^31 bytes, which the host checks), and a tile is a byte offset in
 // the lanes' offsets: range-checked like them, so rows past the end still
 // read zeros, and a tile change needs no new descriptor.
@@ -684,18 +681,25 @@ __device__ __forceinline__ Panels whole_panels(const GemmArgs &g, int wave) {
     Panels P;
     P.rA = make_rsrc(g.A, g.M * g.K);
     P.rB = make_rsrc(g.B, g.N * g.K);
-    P.rS = wave < 4 ? make_rsrc(g.sa, g.M * g.KB * 4) : make_rsrc(g.sb, (int64_t)g.NB * g.KB * 4);
+    if (MODE == MODE_MX)
+        P.rS = wave < 4 ? make_rsrc(g.sa, g.M * (g.K / 32)) : make_rsrc(g.sb, g.N * (g.K / 32));
+    else
+        P.rS = wave < 4 ? make_rsrc(g.sa, g.M * g.KB * 4) : make_rsrc(g.sb, (int64_t)g.NB * g.KB * 4);
     return P;
 }
 
 // Tile (m0, n0)'s offsets for whole_panels: A's and B's row panels, and the
 // scales this wave fetches (a_scale rows for waves 0..3, b_scale column
 // blocks for 4..7).
+template <int MODE>
 __device__ __forceinline__ TileOff tile_off(const GemmArgs &g, int64_t m0, int64_t n0, int wave) {
     TileOff t;
     t.a = (int)(m0 * g.K);
     t.b = (int)(n0 * g.K);
-    t.s = wave < 4 ? (int)(m0 * g.KB * 4) : (int)((n0 / 128) * g.KB * 4);
+    if (MODE == MODE_MX)
+        t.s = (int)((wave < 4 ? m0 : n0) * (g.K / 32));
+    else
+        t.s = wave < 4 ? (int)(m0 * g.KB * 4) : (int)((n0 / 128) * g.KB * 4);
     return t;
 }
 
@@ -909,12 +913,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g) {
         }
         int kb = 0;
         if (KB & 1) {
-            kblock_mx<0>(acc, a, bf, x, L, 0, KB, wm, wn, frow, gq);
+            kblock_mx<0>(acc, a, bf, x, L, 1, 1 < KB, wm, wn, frow, gq);
             kb = 1;
         }
         for (; kb < KB; kb += 2) {
-            kblock_mx<1>(acc, a, bf, x, L, kb, KB, wm, wn, frow, gq);
-            kblock_mx<0>(acc, a, bf, x, L, kb + 1, KB, wm, wn, frow, gq);
+            kblock_mx<1>(acc, a, bf, x, L, kb + 1, kb + 1 < KB, wm, wn, frow, gq);
+            kblock_mx<0>(acc, a, bf, x, L, kb + 2, kb + 2 < KB, wm, wn, frow, gq);
         }
     } else {
 
@@ -1068,16 +1072,15 @@ __device__ __forceinline__ void kblock_first(v4f (&acc)[TM][TN], v4f (&p)[4], fl
 // b + 2G, ... (G = grid size, a multiple of 8, so every tile stays on the XCD
 // the non-persistent mapping gives it).  The K blocks of successive tiles form
 // one stream; block 0 of every tile sits in stage 1, its last block in stage
-// 0.  Blockscale: the descriptors cover whole matrices, so the last K block
-// of a tile DMAs the next tile's block 0 (its lanes' offsets moved by dn) as
-// any block DMAs its successor, and reads its head; a plain tile then stores
-// half of its row groups at once and the other half inside the next tile's
-// first K block (kblock_first), between its MFMAs; the last tile and tiles
-// that are not plain store everything at once.  (Switching descriptors
-// inside the K loop instead made the compiler spill hundreds of VGPRs.)
-// mxfp8: after the last K block, the next tile's block 0 is DMA'd into stage
-// 1, the epilogue stores C from the accumulators behind that DMA, and the
-// stores drain under the next tile's first K block.
+// 0.  The descriptors cover whole matrices, so the last K block of a tile
+// DMAs the next tile's block 0 (its lanes' offsets moved by dn) as any block
+// DMAs its successor, and reads its head.  (Switching descriptors inside the
+// K loop instead made the compiler spill hundreds of VGPRs.)  Blockscale: a
+// plain tile then stores half of its row groups at once and the other half
+// inside the next tile's first K block (kblock_first), between its MFMAs.
+// mxfp8: a plain tile stores all of them at once, and they drain under the
+// next tile's first K block.  The last tile and tiles that are not plain
+// store everything at once.
 // The blockscale kernel runs one copy of this body per row half of the wave
 // grid (WMC = wm, a compile-time constant: each wave executes straight-line
 // code with its row offsets folded), and the second half issues its K
@@ -1105,12 +1108,8 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 
     Loader L;
     init_loader<MODE>(L, g, wave, lane);
-    if constexpr (MX) {
-        L.P = panels_of<MODE>(g, m0, n0, wave);
-    } else {
-        L.P = whole_panels<MODE>(g, wave);
-        shift_loader(L, tile_off(g, m0, n0, wave));
-    }
+    L.P = whole_panels<MODE>(g, wave);
+    shift_loader(L, tile_off<MODE>(g, m0, n0, wave));
 
     v4f acc[TM][TN];
 #pragma unroll
@@ -1159,19 +1158,22 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
         dn = TileOff{0, 0, 0};
         if (has_next) {
-            const TileOff tn = tile_off(gt, m0n, n0n, wave), tc = tile_off(gt, m0, n0, wave);
+            const TileOff tn = tile_off<MODE>(gt, m0n, n0n, wave), tc = tile_off<MODE>(gt, m0, n0, wave);
             dn.a = __builtin_amdgcn_readfirstlane(tn.a - tc.a);
             dn.b = __builtin_amdgcn_readfirstlane(tn.b - tc.b);
             dn.s = __builtin_amdgcn_readfirstlane(tn.s - tc.s);
         }
     };
-    if constexpr (!MX) find_next();
+    find_next();
     for (;;) {
         if constexpr (MX) {
+            const TileOff d0 = {0, 0, 0};
             for (int kb = 0; kb < KB; kb += 2) {
-                kblock_mx<1>(acc, a, bf, x, L, kb, KB, wm, wn, frow, gq);
-                kblock_mx<0>(acc, a, bf, x, L, kb + 1, KB, wm, wn, frow, gq);
+                kblock_mx<1>(acc, a, bf, x, L, kb + 1, true, wm, wn, frow, gq);
+                kblock_mx<0>(acc, a, bf, x, L, kb + 2 < KB ? kb + 2 : 0, kb + 2 < KB || has_next, wm, wn,
+                             frow, gq, kb + 2 < KB ? d0 : dn);
             }
+            shift_loader(L, dn);
         } else {
             {
                 const GemmArgs gt = args();
@@ -1194,18 +1196,6 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
             }
             shift_loader(L, dn);
         }
-        // mxfp8: the next tile's block 0 goes to stage 1 (unread after the
-        // last block's barrier but for head reads whose values are never
-        // used) while this tile's epilogue stores
-        if constexpr (MX) {
-            const GemmArgs gt = args();
-            has_next = __builtin_amdgcn_readfirstlane((int)tile_of(gt, vb + (int)gridDim.x, m0n, n0n));
-            if (has_next) {
-                L.P = panels_of<MODE>(gt, m0n, n0n, wave);
-                load_stage<1>(L, 0);
-            }
-        }
-
         if constexpr (!MX) {
             // the last three products of the tile (kblock_first carries none)
 #pragma unroll
@@ -1213,12 +1203,12 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         }
 
         if constexpr (MX) {
-            // The last tile and tiles that are not plain store here.  Every
-            // other tile stores its 2 * TM pieces behind the next tile's DMA
-            // (other tiles issue the same instructions through the zero-size
-            // descriptor, so that the count is exact on every path): once no
-            // more than those are outstanding, the DMA has landed, and the
-            // stores drain under the next tile's first K block.
+            // The last tile and tiles that are not plain store here; a plain
+            // one stores its 2 * TM pieces per lane (other tiles issue the
+            // same instructions through the zero-size descriptor, so that
+            // every path issues the same vector memory operations), and they
+            // drain under the next tile's first K block, whose block 0 and
+            // head are already in.
             const bool plain = tile_is_plain(args(), m0, n0);
             if (!has_next || !plain) store_tile<MODE>(acc, args(), m0, n0, wave, lane);
             if (!has_next) break;
@@ -1230,10 +1220,6 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
 #pragma unroll
                 for (int i = 0; i < TM; i++) plain_store_rg(acc, i, rT, gt.N, o);
             }
-            static_assert(2 * TM == 16, "the wait below is vmcnt(16)");
-            __builtin_amdgcn_s_waitcnt(0x4F70);   // vmcnt(16): vmcnt[5:4] sit in bits 15:14
-            barrier_lds_only();
-            read_head_mx<1>(a, bf, x, wm, wn, frow, gq);
 #pragma unroll
             for (int i = 0; i < TM; i++)
 #pragma unroll
@@ -1264,7 +1250,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
         vb += (int)gridDim.x;
         m0 = m0n;
         n0 = n0n;
-        if constexpr (!MX) find_next();
+        find_next();
     }
 }
 
@@ -1383,7 +1369,8 @@ int bs_launch_mxgemm(const uint8_t *A, const uint8_t *sa, const uint8_t *B, cons
                      uint16_t *C, int64_t M, int64_t N, int64_t K, int64_t band_rows,
                      int64_t band_stride, hipStream_t stream) {
     const GemmArgs g = gemm_args(A, sa, B, sb, C, M, N, K, band_rows, band_stride);
-    if (g.KB % 2 == 0)
+    const int64_t lim = 0x7FFFFFFF;   // as for the blockscale kernel
+    if (g.KB % 2 == 0 && (M + BM) * K <= lim && (N + BN) * K <= lim)
         return bs_enqueue(mxgemm_persistent_kernel, dim3(persistent_grid(g, stream)), dim3(NTHREADS),
                           stream, g);
     return bs_enqueue(mxgemm_tile_kernel, dim3(gemm_grid(g)), dim3(NTHREADS), stream, g);

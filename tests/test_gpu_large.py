@@ -1,7 +1,7 @@
 """Maximum-size cases on the device (an MI355X holds 288 GB): the dequantizer
 past 2^31 packs, where it switches to 64-bit indices, the GEMM with a
 14 GiB output written as 8 bands, where row offsets pass 2^32 bytes, and the
-GEMM with an operand of more than 2^31 bytes.  Inputs
+GEMMs (blockscale and mxfp8) with an operand of more than 2^31 bytes.  Inputs
 are drawn on the device; sampled outputs (whole rows for the GEMM) are
 checked against the oracle, so nothing large crosses to the host."""
 import numpy as np
@@ -11,7 +11,7 @@ import torch
 import block_scaled_fp8_bsgemm_amd as bs
 import oracle
 import synth
-from gpuutil import bits16, device, gemm_accept_rows, say
+from gpuutil import bits16, device, gemm_accept_rows, mx_accept, say
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +95,35 @@ def test_gemm_operand_past_2gib():
     del C, qa, sa
     torch.cuda.empty_cache()
     gemm_accept_rows(got, np.arange(rows.size), qa_r, sa_r, qb_h, sb_h, f"M={M} {rows.size} whole rows")
+
+
+def test_mxgemm_operand_past_2gib():
+    """The mxfp8 GEMM with an A of more than 2^31 bytes (M = 2^20 + 128,
+    K = 2048), which the host also sends to the tile kernel.  Whole rows on
+    both sides of byte 2^31 of A against O11."""
+    M, N, K = (1 << 20) + 128, 256, 2048
+    dev = device()
+    say(f"mxgemm_fp8 M={M} N={N} K={K} (A of {M * K} bytes)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(24)
+    qa = torch.randint(0, 0x7F, (M, K), dtype=torch.uint8, device=dev, generator=g)   # no NaN codes
+    qa |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    ea = torch.randint(117, 128, (M, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    qb = torch.randint(0, 0x7F, (N, K), dtype=torch.uint8, device=dev, generator=g)
+    qb |= torch.randint(0, 2, (N, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    eb = torch.randint(117, 128, (N, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    C.view(torch.int16).fill_(0x7FC0)
+    bs.mxgemm_fp8(qa, ea, qb, eb, C)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    split = (1 << 31) // K
+    edge = [0, split - 1, split, split + 1, M - 129, M - 128, M - 1]
+    rows = np.unique(np.concatenate([rng.integers(0, M, 40), edge])).astype(np.int64)
+    tm = torch.from_numpy(rows).to(dev)
+    got = C.view(M, N)[tm].view(torch.int16).cpu().numpy().view(np.uint16)
+    qa_r, ea_r = qa[tm].cpu().numpy(), ea[tm].cpu().numpy()
+    qb_h, eb_h = qb.cpu().numpy(), eb.cpu().numpy()
+    del C, qa, ea
+    torch.cuda.empty_cache()
+    mx_accept(got, qa_r, ea_r, qb_h, eb_h, f"mx M={M} {rows.size} whole rows", model=False)
