@@ -17,8 +17,8 @@
 //    in LDS, double buffered (2 x 64 KiB); rows are placed in even / odd
 //    128-byte slots and 16-byte chunks XOR-swizzled (swz) so that every MFMA
 //    operand read is served without bank conflicts;
-//  - global loads use buffer descriptors sized to the matrix, so rows past M
-//    (a ragged last tile) read as zero without any branch;
+//  - global loads use buffer descriptors that end where the matrix ends, so
+//    rows past M (a ragged last tile) read as zero without any branch;
 //  - waves form a 2 (M) x 4 (N) grid of 128 x 64 wave tiles (8 x 4 MFMA
 //    sub-tiles, 128 fp32 accumulator registers per lane);
 //  - the MFMA takes the B fragment as its first operand, so each lane ends up
@@ -37,11 +37,13 @@
 //    panels in that XCD's L2 (its 32 concurrent tiles span 4 M-tiles x 8
 //    N-tiles; measured faster than 8 x 4, 2 x 16 or 1 x 32).
 //
-// When K / 128 is even (the benchmark's K = 2048), the blockscale and mxfp8
-// GEMMs run as persistent kernels instead: one workgroup per CU walks several
-// tiles, so the workgroup launch is not paid per tile.  In the blockscale one
-// a finished tile's stores go out while the next tile's first operands land
-// and inside its first K block, between its MFMAs (bit-identical results).
+// When K / 128 is even (the benchmark's K = 2048) and each operand stays
+// under 2^31 bytes, the blockscale and mxfp8 GEMMs run as persistent kernels
+// instead: one workgroup per CU walks several tiles, so the workgroup launch
+// is not paid per tile, a tile's last K block already loads the next tile's
+// first, and a finished tile's stores drain under the next tile's first K
+// block (in the blockscale one, half of them go out between its MFMAs).
+// Results are bit-identical to the tile kernels'.
 //
 // A second blockscale kernel reads B in a prepacked form (the same bytes in the
 // MFMA's operand order, written once by bprepack_kernel) straight into
@@ -622,8 +624,8 @@ __device__ __forceinline__ bool tile_of(const GemmArgs &g, int b, int64_t &m0, i
     return true;
 }
 
-// The tile-dependent part of the loader: descriptors of the tile's row panels
-// and scales, zero past the end of the matrices.
+// The tile-dependent part of the loader in the tile kernels: descriptors of
+// the tile's row panels and scales, zero past the end of the matrices.
 template <int MODE>
 __device__ __forceinline__ Panels panels_of(const GemmArgs &g, int64_t m0, int64_t n0, int wave) {
     const int64_t K = g.K;
@@ -1147,9 +1149,9 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &g) {
     // that tile's origin
     bool pend = false;
     int64_t pm0 = 0, pn0 = 0;
-    // the tile after this one and, blockscale, the move of the loader's
-    // offsets from this tile to it (zero if there is none); found at the
-    // tile boundary, so that only three offsets stay live across the K loop
+    // the tile after this one and the move of the loader's offsets from
+    // this tile to it (zero if there is none); found at the tile boundary,
+    // so that only three offsets stay live across the K loop
     int64_t m0n = 0, n0n = 0;
     bool has_next = false;
     TileOff dn = {0, 0, 0};
