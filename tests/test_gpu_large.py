@@ -65,6 +65,44 @@ def test_gemm_output_past_4gib():
     gemm_accept_rows(got, rows, qa_h, sa_h, qb_h, sb_h, f"M={M} {rows.size} whole rows")
 
 
+def test_gemm_persistent_offsets_near_2gib():
+    """The largest A the persistent kernel takes at K = 2048: (M + 256) * K
+    just under 2^31, so its lanes' byte offsets, ragged tile rows included,
+    come within one tile of 2^31.  Whole rows at both ends against the
+    oracle (both GEMMs)."""
+    M, N, K = (1 << 20) - 384, 512, 2048
+    assert (M + 256) * K <= 0x7FFFFFFF < (M + 384) * K   # the largest M (a multiple of 128) it takes
+    KB = K // 128
+    dev = device()
+    say(f"bsgemm_fp8 / mxgemm_fp8 M={M} N={N} K={K} (A of {M * K} bytes, persistent)")
+    g = torch.Generator(device=dev)
+    g.manual_seed(25)
+    qa = torch.randint(0, 0x7F, (M, K), dtype=torch.uint8, device=dev, generator=g)   # no NaN codes
+    qa |= torch.randint(0, 2, (M, K), dtype=torch.uint8, device=dev, generator=g) << 7
+    sa = torch.rand((M, KB), device=dev, generator=g) * 2.0 ** -8
+    ea = torch.randint(117, 128, (M, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    qb, sb = bs.blockq_e4m3(0.02 * torch.randn(N, K, device=dev, generator=g), 128)
+    eb = torch.randint(117, 128, (N, K // 32), dtype=torch.uint8, device=dev, generator=g)
+    C = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    C2 = torch.empty(M * N, dtype=torch.bfloat16, device=dev)
+    C.view(torch.int16).fill_(0x7FC0)
+    C2.view(torch.int16).fill_(0x7FC0)
+    bs.bsgemm_fp8(qa, sa, qb, sb, C)
+    bs.mxgemm_fp8(qa, ea, qb, eb, C2)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 24), [0, 1, M - 257, M - 256, M - 2, M - 1]])).astype(np.int64)
+    tm = torch.from_numpy(rows).to(dev)
+    got = C.view(M, N)[tm].view(torch.int16).cpu().numpy().view(np.uint16)
+    got2 = C2.view(M, N)[tm].view(torch.int16).cpu().numpy().view(np.uint16)
+    qa_r, sa_r, ea_r = qa[tm].cpu().numpy(), sa[tm].cpu().numpy(), ea[tm].cpu().numpy()
+    qb_h, sb_h, eb_h = qb.cpu().numpy(), sb.cpu().numpy(), eb.cpu().numpy()
+    del C, C2, qa, sa, ea
+    torch.cuda.empty_cache()
+    gemm_accept_rows(got, np.arange(rows.size), qa_r, sa_r, qb_h, sb_h, f"M={M} {rows.size} whole rows")
+    mx_accept(got2, qa_r, ea_r, qb_h, eb_h, f"mx M={M} {rows.size} whole rows", model=False)
+
+
 def test_gemm_operand_past_2gib():
     """A of 2^31 bytes and more (M = 2^20 + 128, K = 2048): past what one
     31-bit descriptor offset reaches, so the host takes the tile kernel,
