@@ -287,6 +287,18 @@ __device__ __forceinline__ int sa_row(int p) {
     return (q >> 4) * WM + i * 16 + (q & 15);
 }
 
+// The mxfp8 scale slots (4 bytes each: a row's scale bytes of the K block)
+// hold the tile's 256 A rows, then its 256 B rows, so that the 8 A rows of a
+// lane (row 128 wm + 16 i + frow, i = 0..7) sit in 8 consecutive slots, and
+// so do its 4 B rows (the B rows of LDS rows 64 wn + 16 j + frow, j = 0..3):
+// three 16-byte reads instead of twelve byte reads.  Slot p (waves 0..3 fill
+// 0..255, waves 4..7 256..511) holds tile row mx_scale_row(p) of A or B.
+__device__ __forceinline__ int mx_scale_row(int p) {
+    if (p < BM) return (p & 128) | ((p & 7) << 4) | ((p >> 3) & 15);
+    const int q = p - BM;
+    return brow_of((q & ~63) | ((q & 3) << 4) | ((q >> 2) & 15));
+}
+
 template <int ST>
 __device__ __forceinline__ void read_scales(RawScales &r, int wm, int wn, int frow) {
     const float *sc = stS<ST>();
@@ -333,26 +345,28 @@ struct MxScales {
     int b;           // B rows of its 4 column groups
 };
 
-__device__ __forceinline__ int pack4(int b0, int b1, int b2, int b3) {
-    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+// byte g of each of the four dwords of v, packed (byte i from dword i)
+__device__ __forceinline__ int byte_g4(const u32x4 &v, int g) {
+    // v_perm selects bytes of {hi, lo}: selector byte k in 0..7 picks that
+    // byte, 0x0C gives 0
+    const uint32_t s01 = 0x0C0C0400u + (uint32_t)g * 0x0101u;            // bytes g, 4 + g
+    const uint32_t s23 = 0x04000C0Cu + (uint32_t)g * 0x01010000u;        // bytes 2, 3
+    const uint32_t t01 = __builtin_amdgcn_perm(v[1], v[0], s01);
+    const uint32_t t23 = __builtin_amdgcn_perm(v[3], v[2], s23);
+    return (int)(t01 | t23);
 }
 
 template <int ST>
 __device__ __forceinline__ void read_mx_scales(MxScales &x, int wm, int wn, int frow, int g) {
+    // the slots of the lane's 8 A rows and of its 4 B rows are contiguous
+    // (mx_scale_row): 32 and 16 bytes, each dword a row's 4 group bytes
     const uint8_t *sc = (const uint8_t *)stS<ST>();
-    int v[TM];
-#pragma unroll
-    for (int i = 0; i < TM; i++) v[i] = sc[(wm * WM + i * 16 + frow) * 4 + g];
-    x.a[0] = pack4(v[0], v[1], v[2], v[3]);
-    x.a[1] = pack4(v[4], v[5], v[6], v[7]);
-    int w[TN];
-#pragma unroll
-    for (int j = 0; j < TN; j++) {
-        // B row brow_of(wn * WN + 16 j + frow): a lane base plus 0, 4, 32, 36
-        const int bro = BM + wn * WN + 8 * (frow >> 2) + (frow & 3) + 32 * (j >> 1) + 4 * (j & 1);
-        w[j] = sc[bro * 4 + g];
-    }
-    x.b = pack4(w[0], w[1], w[2], w[3]);
+    const u32x4 a0 = *(const u32x4 *)(sc + (wm * WM + frow * 8) * 4);
+    const u32x4 a1 = *(const u32x4 *)(sc + (wm * WM + frow * 8) * 4 + 16);
+    const u32x4 b = *(const u32x4 *)(sc + (BM + wn * WN + frow * 4) * 4);
+    x.a[0] = byte_g4(a0, g);
+    x.a[1] = byte_g4(a1, g);
+    x.b = byte_g4(b, g);
 }
 
 // The scaled MFMA of A row group i and B column group j (both compile-time
@@ -668,8 +682,9 @@ __device__ __forceinline__ void init_loader(Loader &L, const GemmArgs &g, int wa
     L.voffB = rowB * K + chunk * 16;
     L.voffB1 = L.voffB ^ 64;
     L.k4 = 4 * K;
-    // blockscale: waves 0..3 fetch a_scale in the slot order of sa_row
-    L.soff = MODE == MODE_MX ? ((wave & 3) * 64 + lane) * (K / 32)
+    // blockscale: waves 0..3 fetch a_scale in the slot order of sa_row;
+    // mxfp8: each row's 4 scale bytes in the slot order of mx_scale_row
+    L.soff = MODE == MODE_MX ? mx_scale_row(wave * 64 + lane) * (K / 32)
                              : (wave < 4 ? sa_row(wave * 64 + lane) : lane) * g.KB * 4;
     L.sdst = wave * 256;
 }
